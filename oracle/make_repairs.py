@@ -15,7 +15,7 @@ TEST INFRASTRUCTURE ONLY (see the package header).
 import math
 import sys
 import time
-from concurrent.futures import ThreadPoolExecutor
+from concurrent.futures import ProcessPoolExecutor
 
 from synth import CONFIGS
 from synth.generate import generate_head, head_field, q_block_bits, save_repairs
@@ -71,14 +71,21 @@ def repair_head(spec, cuts, thr, b, h):
     return repairs
 
 
-def make(cfg_id, threads=8):
+def _job(args):
+    spec, cuts, thr, b, h = args
+    return repair_head(spec, cuts, thr, b, h)
+
+
+def make(cfg_id, workers=8):
     specs = [s for s in CONFIGS.values() if s.cfg_id == cfg_id]
     spec = specs[0]
     cuts, thr = boundaries_for(specs, spec.nb)
     t0 = time.time()
     jobs = [(b, h) for b in range(spec.B) for h in range(spec.H)]
-    with ThreadPoolExecutor(max_workers=threads) as ex:
-        parts = list(ex.map(lambda bh: repair_head(spec, cuts, thr, *bh), jobs))
+    # One process per worker: numpy's BLAS must not be entered from several
+    # threads of one process at once (concurrent calls corrupt results).
+    with ProcessPoolExecutor(max_workers=workers) as ex:
+        parts = list(ex.map(_job, [(spec, cuts, thr, b, h) for b, h in jobs]))
     repairs = {}
     for p in parts:
         repairs.update(p)

@@ -50,7 +50,11 @@ def f32_to_bf16_bits(x):
 
 
 def _field(spec: Spec, stream_key, lo=0, hi=None):
-    """Sum of 8 random-Fourier modes over tokens [lo, hi) of the grid, float32 [hi - lo, d]."""
+    """Sum of 8 random-Fourier modes over tokens [lo, hi) of the grid, float32 [hi - lo, d].
+
+    Elementwise numpy only (no BLAS), accumulated mode by mode in a fixed
+    order, so the values do not depend on threading.
+    """
     if hi is None:
         hi = spec.N
     T, Y, X = spec.grid
@@ -59,14 +63,21 @@ def _field(spec: Spec, stream_key, lo=0, hi=None):
     amp = rng.normal(0.0, 0.5, size=(_N_MODES, spec.d))
     ph = rng.uniform(0.0, 2.0 * np.pi, size=(_N_MODES, spec.d))
     n = np.arange(lo, hi, dtype=np.int64)
-    x = n % X
-    y = (n // X) % Y
-    t = n // (X * Y)
-    pos = np.stack([t / T, y / Y, x / X], axis=1)            # [n, 3]
-    theta = 2.0 * np.pi * (pos @ u.T)                        # [n, 8]
-    basis = np.concatenate([np.cos(theta), np.sin(theta)], axis=1)          # [n, 16]
-    weights = np.concatenate([amp * np.cos(ph), -amp * np.sin(ph)], axis=0)  # [16, d]
-    return (basis @ weights).astype(np.float32)
+    x = (n % X) / X
+    y = ((n // X) % Y) / Y
+    t = (n // (X * Y)) / T
+    wc = amp * np.cos(ph)                                   # [8, d]
+    ws = amp * np.sin(ph)
+    out = np.zeros((hi - lo, spec.d), dtype=np.float64)
+    tmp = np.empty_like(out)
+    for f in range(_N_MODES):
+        theta = 2.0 * np.pi * (u[f, 0] * t + u[f, 1] * y + u[f, 2] * x)   # [n]
+        # a cos(theta + ph) = (a cos ph) cos theta - (a sin ph) sin theta
+        np.multiply(np.cos(theta)[:, None], wc[f][None, :], out=tmp)
+        out += tmp
+        np.multiply(np.sin(theta)[:, None], ws[f][None, :], out=tmp)
+        out -= tmp
+    return out.astype(np.float32)
 
 
 def head_field(spec: Spec, b: int, h: int):
