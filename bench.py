@@ -1,0 +1,267 @@
+"""Benchmark of the block-sparse attention layer on one MI355X.
+
+Workload: the Wan-14B-like layer (B=1, H=40, N=75600 = 21 x 45 x 80 tokens,
+d=128, 128-token blocks), top-k key tiles at 95% sparsity, bf16 inputs from
+the seeded generator (already resident in HBM when timing starts).
+
+A step is one pass of the whole path: pool + classify, list compaction,
+sparse attention (bf16 output written directly: this workload has no
+marginal tiles, so the linear branch and the sum are empty).
+
+Printed JSON line:
+  value        kept-block attention FLOP per step / step time (TFLOP/s),
+               i.e. whole-layer effective throughput;
+  roofline     the sparse-attention kernel alone: kept FLOP per launch /
+               its average launch time (HIP events on its stream) against
+               the bf16 dense MFMA peak;
+  cpu_baseline the fp64 oracle on the host cores on a bounded sample;
+  extra        per-stage times, dense baselines (this library's dense kernel
+               and torch SDPA) and ms/layer ratios.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--config wan14b]
+                [--no-cpu-baseline] [--no-dense] [--profile]
+"""
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kept_flop(crit_idx, crit_cnt, N, block, d):
+    """Exact kept-pair FLOP: 4 * rows(i) * keys(j) * d over every kept pair."""
+    import torch
+    nb = crit_idx.shape[-1]
+    width = crit_idx.shape[-1]
+    nqb = crit_idx.shape[-2]
+    valid = torch.arange(width, device=crit_idx.device) < crit_cnt[..., None]
+    j = torch.where(valid, crit_idx, torch.zeros_like(crit_idx)).long()
+    keys = torch.clamp(N - j * block, max=block)
+    keys = torch.where(valid, keys, torch.zeros_like(keys))
+    rows = torch.clamp(N - torch.arange(nqb, device=j.device) * block, max=block)
+    per = (keys.sum(-1) * rows).sum().item()
+    del nb
+    return 4.0 * per * d
+
+
+def cpu_baseline(spec, data, kc, km, budget_s=20.0):
+    """Time the fp64 oracle on a bounded sample of the workload on the host cores."""
+    from oracle import sla as osla
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    sel = "sla3" if spec.mode == "maskin" else spec.mode
+    flop = 0.0
+    blocks = 0
+    t0 = time.perf_counter()
+    g = np.random.default_rng(0)
+    h = 0
+    while time.perf_counter() - t0 < budget_s and h < spec.H:
+        q = osla.bf16_to_f64(data["q"][0, h])[None, None]
+        k = osla.bf16_to_f64(data["k"][0, h])[None, None]
+        v = osla.bf16_to_f64(data["v"][0, h])[None, None]
+        cls, *_ = osla.class_map(q, k, spec.block, sel, spec.keep, spec.marg, spec.thr)
+        rows = [(0, 0, int(i)) for i in g.choice(spec.nb, size=16, replace=False)]
+        osla.forward_rows(q, k, v, cls, spec.block, rows)
+        for (_, _, i) in rows:
+            lo, hi = osla.block_bounds(spec.N, spec.block, i)
+            for j in np.nonzero(cls[0, 0, i] == osla.CRITICAL)[0]:
+                klo, khi = osla.block_bounds(spec.N, spec.block, int(j))
+                flop += 4.0 * (hi - lo) * (khi - klo) * spec.d
+        blocks += len(rows)
+        h += 1
+    dt = time.perf_counter() - t0
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": (f"fp64 numpy oracle: pool + score + top-k class map of {h} head(s) in full, "
+                       f"then masked softmax attention of {blocks} sampled query blocks "
+                       f"({16} per head); kept-block FLOP of those blocks / wall time "
+                       f"({dt:.1f} s)")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="wan14b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--profile", action="store_true", help="short run for a profiler")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path shards by "
+              "head with no communication inside attention, so run one process per GPU instead.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.profile:
+        args.no_cpu_baseline = True
+        args.no_dense = True
+
+    import torch
+    import block_sparse_attention_meanpool_amd as sla
+    from synth import CONFIGS, generate
+
+    spec = CONFIGS[args.config]
+    B, H, N, d, b, nb = spec.B, spec.H, spec.N, spec.d, spec.block, spec.nb
+    sel = "sla3" if spec.mode == "maskin" else spec.mode
+    kc, km = sla.counts_for(sel, nb, spec.keep, spec.marg)
+    log(f"[bench] {spec.name}: B={B} H={H} N={N} d={d} block={b} nb={nb} k_crit={kc} k_marg={km}")
+    t0 = time.time()
+    data = generate(spec)
+    log(f"[bench] generated inputs in {time.time() - t0:.1f} s")
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(data[t].view(np.int16)).view(torch.bfloat16).to(dev) for t in "qkv")
+    torch.cuda.synchronize()
+
+    # every buffer allocated once, outside the timed region
+    cls = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=dev)
+    ws = torch.empty(sla.lib().sla_pool_classify_ws_bytes(B, H, N, d, b, 0), dtype=torch.uint8,
+                     device=dev)
+    kc_max = nb if sel == "cdf" else kc
+    crit_idx = torch.empty((B, H, nb, kc_max), dtype=torch.int32, device=dev)
+    crit_cnt = torch.empty((B, H, nb), dtype=torch.int32, device=dev)
+    marg_idx = marg_cnt = o_s = o_lin = lin_ws = None
+    if km:
+        marg_idx = torch.empty((B, H, nb, km), dtype=torch.int32, device=dev)
+        marg_cnt = torch.empty((B, H, nb), dtype=torch.int32, device=dev)
+        o_s = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        o_lin = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        lin_ws = torch.empty(sla.lib().sla_linear_branch_ws_bytes(B, H, N, d, b), dtype=torch.uint8,
+                             device=dev)
+    o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    stages = ["pool_classify", "block_mask", "sparse_attn"] + (["linear_branch", "combine"] if km else [])
+    ev = {s: [] for s in stages}
+
+    def step(record):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)] if record else None
+        if record:
+            marks[0].record(stream)
+        sla.sla_pool_classify(q, k, b, sel, kc, km, spec.thr or 0.0, cls=cls, ws=ws)
+        if record:
+            marks[1].record(stream)
+        sla.sla_block_mask(cls, kc_max, km, crit_idx, crit_cnt, marg_idx, marg_cnt)
+        if record:
+            marks[2].record(stream)
+        if km:
+            sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt, o_s=o_s)
+            if record:
+                marks[3].record(stream)
+            sla.sla_linear_branch_fwd(q, k, v, b, marg_idx, marg_cnt, o_lin=o_lin, ws=lin_ws)
+            if record:
+                marks[4].record(stream)
+            sla.sla_combine(o_s, o_lin, o=o)
+            if record:
+                marks[5].record(stream)
+        else:
+            sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt, o_s=o)
+            if record:
+                marks[3].record(stream)
+        if record:
+            ev_list.append(marks)
+
+    ev_list = []
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup} steps done")
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    for marks in ev_list:
+        for i, s in enumerate(stages):
+            ev[s].append(marks[i].elapsed_time(marks[i + 1]))
+    ms_step = wall * 1e3 / args.steps
+    stage_ms = {s: float(np.mean(ev[s])) for s in stages}
+    stage_min = {s: float(np.min(ev[s])) for s in stages}
+    log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
+
+    flop = kept_flop(crit_idx, crit_cnt, N, b, d) * B
+    kept_frac = crit_cnt.double().mean().item() / nb
+    sparse_ms = stage_ms["sparse_attn"]
+    achieved = flop / (sparse_ms * 1e-3) / 1e12
+    value = flop / (ms_step * 1e-3) / 1e12
+    pool_bytes = 2 * B * H * N * d * 2 + 2 * B * H * nb * d * 4
+    extra = {
+        "stage_ms_mean": stage_ms, "stage_ms_min": stage_min,
+        "kept_fraction": kept_frac, "kept_flop_per_step": flop,
+        "sparse_kernel_tflops": achieved,
+        "pool_classify_gbs_algorithmic": pool_bytes / (stage_ms["pool_classify"] * 1e-3) / 1e9,
+    }
+
+    if not args.no_dense:
+        od = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        sla.sla_dense_attn_fwd(q, k, v, b, o=od)
+        torch.cuda.synchronize()
+        reps = 2
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            sla.sla_dense_attn_fwd(q, k, v, b, o=od)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dense_ms = e0.elapsed_time(e1) / reps
+        dense_flop = 4.0 * B * H * N * N * d
+        extra["dense_kernel_ms"] = dense_ms
+        extra["dense_kernel_tflops"] = dense_flop / (dense_ms * 1e-3) / 1e12
+        del od
+        try:
+            import torch.nn.functional as Fn
+            from torch.nn.attention import SDPBackend, sdpa_kernel
+            # flash / memory-efficient kernels only: never the bf16 math path
+            with torch.no_grad(), sdpa_kernel([SDPBackend.FLASH_ATTENTION,
+                                               SDPBackend.EFFICIENT_ATTENTION]):
+                Fn.scaled_dot_product_attention(q[:, :4], k[:, :4], v[:, :4])
+                torch.cuda.synchronize()
+                e0.record(stream)
+                Fn.scaled_dot_product_attention(q, k, v)
+                e1.record(stream)
+                torch.cuda.synchronize()
+            extra["torch_sdpa_ms"] = e0.elapsed_time(e1)
+            extra["torch_sdpa_tflops"] = dense_flop / (extra["torch_sdpa_ms"] * 1e-3) / 1e12
+        except Exception as exc:  # context only
+            extra["torch_sdpa_error"] = str(exc)[:200]
+        best_dense = min(x for x in (extra.get("dense_kernel_ms"), extra.get("torch_sdpa_ms")) if x)
+        extra["dense_best_ms"] = best_dense
+        extra["speedup_vs_best_dense"] = best_dense / ms_step
+        log(f"[bench] dense: ours {extra['dense_kernel_ms']:.2f} ms, sdpa {extra.get('torch_sdpa_ms')}")
+
+    result = {
+        "metric": "effective attn TFLOP/s on kept blocks; ms/layer vs dense at 95% sparsity",
+        "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic (seeded random-Fourier video-latent fields + noise)",
+        "config": {"workload": f"{spec.name}: B={B} H={H} N={N} (21x45x80) d={d} block={b}, "
+                               f"top-{kc} of {nb} key tiles per query block (95% sparsity)",
+                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+        "extra": extra,
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host cores")
+        result["cpu_baseline"] = cpu_baseline(spec, data, kc, km)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+// C ABI: host-side validation, workspace layout and kernel launches.
+// Every entry point checks all arguments before enqueueing anything.
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+#include "../../include/sla.h"
+#include "launch.h"
+
+namespace {
+
+constexpr int64_t kMaxBlocks = 4096;
+constexpr int64_t kMaxHeads = 65535;  // B*H: grid y/z extent of the pooling and score launches
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Shapes shared by every call.  On success *nb is ceil(N / block).
+sla_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block, int64_t* nb) {
+  if (B < 1 || H < 1 || N < 1) return SLA_ERR_INVALID_ARG;
+  if ((d != 64 && d != 128) || (block != 64 && block != 128)) return SLA_ERR_UNSUPPORTED;
+  if (B * H > kMaxHeads) return SLA_ERR_UNSUPPORTED;
+  const int64_t n = (N + block - 1) / block;
+  if (n > kMaxBlocks) return SLA_ERR_UNSUPPORTED;
+  // one head's tensor must fit the 31-bit range of a buffer resource, with a
+  // block of slack for the rows of a partial last block
+  if ((N + block) * d * 2 > INT32_MAX) return SLA_ERR_UNSUPPORTED;
+  if (B * H * n > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
+  *nb = n;
+  return SLA_OK;
+}
+
+sla_status from_hip(hipError_t e) { return e == hipSuccess ? SLA_OK : SLA_ERR_HIP; }
+
+size_t pooled_bytes(int64_t BH, int64_t nb, int64_t d) {
+  return round_up((size_t)(BH * nb * d) * sizeof(float), 256);
+}
+size_t score_bytes(int64_t BH, int64_t nb) {
+  return round_up((size_t)(BH * nb * nb) * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t sla_pool_classify_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block,
+                                  int32_t pooled_given) {
+  int64_t nb = 0;
+  if (check_shape(B, H, N, d, block, &nb) != SLA_OK) return 0;
+  const int64_t BH = B * H;
+  return (pooled_given ? 0 : 2 * pooled_bytes(BH, nb, d)) + score_bytes(BH, nb);
+}
+
+sla_status sla_pool_classify(const uint16_t* q, const uint16_t* k, int64_t B, int64_t H, int64_t N,
+                             int64_t d, int32_t block, int32_t mode, int32_t k_crit, int32_t k_marg,
+                             float thr, float scale, float* q_pool, float* k_pool, uint8_t* cls,
+                             void* ws, size_t ws_bytes, hipStream_t stream) {
+  int64_t nb = 0;
+  sla_status st = check_shape(B, H, N, d, block, &nb);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !cls) return SLA_ERR_INVALID_ARG;
+  if ((q_pool == nullptr) != (k_pool == nullptr)) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_pool) || !aligned16(k_pool))
+    return SLA_ERR_ALIGNMENT;
+  if (mode == SLA_SEL_TOPK || mode == SLA_SEL_SLA3) {
+    if (k_crit < 1 || k_crit > nb) return SLA_ERR_INVALID_ARG;
+    if (mode == SLA_SEL_SLA3 && (k_marg < 0 || k_marg > nb - k_crit)) return SLA_ERR_INVALID_ARG;
+  } else if (mode == SLA_SEL_CDF) {
+    if (!(thr > 0.f && thr < 1.f)) return SLA_ERR_INVALID_ARG;
+  } else {
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
+  const int64_t BH = B * H;
+  const size_t need = sla_pool_classify_ws_bytes(B, H, N, d, block, q_pool != nullptr);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+
+  char* p = static_cast<char*>(ws);
+  float* qp = q_pool;
+  float* kp = k_pool;
+  if (!qp) {
+    qp = reinterpret_cast<float*>(p);
+    kp = reinterpret_cast<float*>(p + pooled_bytes(BH, nb, d));
+    p += 2 * pooled_bytes(BH, nb, d);
+  }
+  float* S = reinterpret_cast<float*>(p);
+  const int kc = mode == SLA_SEL_CDF ? 0 : k_crit;
+  const int km = mode == SLA_SEL_SLA3 ? k_marg : 0;
+
+  st = from_hip(sla::launch_pool(q, k, qp, kp, BH, (int)N, (int)d, block, (int)nb, stream));
+  if (st != SLA_OK) return st;
+  st = from_hip(sla::launch_scores(qp, kp, S, BH, (int)d, (int)nb, scale, stream));
+  if (st != SLA_OK) return st;
+  return from_hip(sla::launch_select(S, cls, BH * nb, (int)nb, mode, kc, km, thr, stream));
+}
+
+sla_status sla_block_mask(const uint8_t* cls, int64_t B, int64_t H, int64_t nqb, int64_t nkb,
+                          int32_t* crit_idx, int32_t* crit_cnt, int32_t kc_max, int32_t* marg_idx,
+                          int32_t* marg_cnt, int32_t km_max, int32_t* err_flag,
+                          hipStream_t stream) {
+  if (!cls || !crit_idx || !crit_cnt) return SLA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || nqb < 1 || nkb < 1 || nkb > kMaxBlocks) return SLA_ERR_INVALID_ARG;
+  if (kc_max < 1 || kc_max > nkb) return SLA_ERR_INVALID_ARG;
+  if ((marg_idx == nullptr) != (marg_cnt == nullptr)) return SLA_ERR_INVALID_ARG;
+  if (marg_idx && (km_max < 1 || km_max > nkb)) return SLA_ERR_INVALID_ARG;
+  if (!marg_idx) km_max = 0;
+  const int64_t rows = B * H * nqb;
+  if ((rows + 3) / 4 > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
+  return from_hip(sla::launch_block_mask(cls, rows, (int)nkb, crit_idx, crit_cnt, kc_max, marg_idx,
+                                         marg_cnt, km_max, err_flag, stream));
+}
+
+sla_status sla_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                               int64_t H, int64_t N, int64_t d, int32_t block,
+                               const int32_t* crit_idx, const int32_t* crit_cnt, int32_t kc_max,
+                               float scale, void* o_s, int32_t o_is_fp32, float* lse,
+                               hipStream_t stream) {
+  int64_t nb = 0;
+  sla_status st = check_shape(B, H, N, d, block, &nb);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !v || !o_s || !crit_idx || !crit_cnt) return SLA_ERR_INVALID_ARG;
+  if (kc_max < 1 || kc_max > nb) return SLA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_s)) return SLA_ERR_ALIGNMENT;
+  return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
+                                   crit_cnt, kc_max, scale, o_s, o_is_fp32 != 0, lse, stream));
+}
+
+sla_status sla_dense_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                              int64_t H, int64_t N, int64_t d, int32_t block, float scale, void* o,
+                              int32_t o_is_fp32, float* lse, hipStream_t stream) {
+  int64_t nb = 0;
+  sla_status st = check_shape(B, H, N, d, block, &nb);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !v || !o) return SLA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SLA_ERR_ALIGNMENT;
+  return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, nullptr, nullptr,
+                                   (int)nb, scale, o, o_is_fp32 != 0, lse, stream));
+}
+
+size_t sla_linear_branch_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {
+  int64_t nb = 0;
+  if (check_shape(B, H, N, d, block, &nb) != SLA_OK) return 0;
+  const int64_t BH = B * H;
+  return round_up((size_t)(BH * nb * d * d) * sizeof(float), 256) +
+         round_up((size_t)(BH * nb * d) * sizeof(float), 256);
+}
+
+sla_status sla_linear_branch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                                 int64_t H, int64_t N, int64_t d, int32_t block,
+                                 const int32_t* marg_idx, const int32_t* marg_cnt, int32_t km_max,
+                                 float* o_lin, void* ws, size_t ws_bytes, hipStream_t stream) {
+  int64_t nb = 0;
+  sla_status st = check_shape(B, H, N, d, block, &nb);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !v || !o_lin || !marg_idx || !marg_cnt) return SLA_ERR_INVALID_ARG;
+  if (km_max < 1 || km_max > nb) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_lin)) return SLA_ERR_ALIGNMENT;
+  const size_t need = sla_linear_branch_ws_bytes(B, H, N, d, block);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  const int64_t BH = B * H;
+  float* Hs = static_cast<float*>(ws);
+  float* Zs = reinterpret_cast<float*>(static_cast<char*>(ws) +
+                                       round_up((size_t)(BH * nb * d * d) * sizeof(float), 256));
+  return from_hip(sla::launch_linear(q, k, v, BH, (int)N, (int)d, block, (int)nb, marg_idx,
+                                     marg_cnt, km_max, o_lin, Hs, Zs, stream));
+}
+
+sla_status sla_combine(const void* o_s, int32_t o_s_is_fp32, const float* o_lin, uint16_t* o,
+                       int64_t n_elems, hipStream_t stream) {
+  if (!o_s || !o || n_elems < 0 || n_elems % 8 != 0) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(o_s) || !aligned16(o_lin) || !aligned16(o)) return SLA_ERR_ALIGNMENT;
+  if ((n_elems / 8 + 255) / 256 > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
+  return from_hip(sla::launch_combine(o_s, o_s_is_fp32 != 0, o_lin, o, n_elems, stream));
+}
+
+const char* sla_status_string(sla_status status) {
+  switch (status) {
+    case SLA_OK: return "ok";
+    case SLA_ERR_INVALID_ARG: return "invalid argument";
+    case SLA_ERR_UNSUPPORTED: return "unsupported shape (d and block must be 64 or 128, nb <= 4096)";
+    case SLA_ERR_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case SLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SLA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int32_t sla_version(void) { return 100; }
+
+}  // extern "C"

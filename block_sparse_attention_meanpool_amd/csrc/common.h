@@ -1,0 +1,121 @@
+// Device helpers shared by the gfx950 kernels of this library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sla {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// Round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end return 0
+// and stores past the end are dropped by the hardware.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// Exchange a value with the lane 32 positions away (lanes l and l^32).
+__device__ __forceinline__ float swap_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + lo + hi of a packed bf16 pair, in one v_dot2 against (1, 1).
+__device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, packed),
+                                         __builtin_bit_cast(bf16x2, 0x3f803f80u), acc, false);
+}
+
+// ---------------------------------------------------------------------------
+// MFMA 32x32x16 lane layout (gfx950, wave64), used throughout:
+//   A (32 x 16, M x K): lane l holds A[l % 32][8 * (l / 32) + 0..7]
+//   B (16 x 32, K x N): lane l holds B[8 * (l / 32) + 0..7][l % 32]
+//   C (32 x 32):        lane l, register r holds C[8*(r/4) + 4*(l/32) + r%4][l % 32]
+// ---------------------------------------------------------------------------
+
+// Row permutation of a 32-row A operand that makes the C registers 0..7 of a
+// lane hold 8 consecutive rows: MFMA row m reads source row swap_bits_2_3(m).
+// Lane half h then holds source rows 8h + r (r = 0..7) in C registers 0..7 and
+// rows 16 + 8h + (r - 8) in registers 8..15.
+__device__ __forceinline__ int swap_bits_2_3(int m) {
+  return (m & 0x13) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// ---------------------------------------------------------------------------
+// Transposed tile in LDS: element (row = feature f, col = token t) of a tile
+// with `T` tokens per row, stored token-contiguous in 16-byte chunks of 8
+// tokens.  Chunk c of row f lives at physical chunk c ^ swz(f), which makes
+// both the 16-lane MFMA operand reads (16 consecutive rows, one chunk) and the
+// 8x8 transpose writes below free of bank conflicts for T = 128.
+// ---------------------------------------------------------------------------
+template <int T>
+__device__ __forceinline__ int tr_swz(int f) {
+  if constexpr (T == 128) return (f & 15) ^ ((f >> 2) & 4);
+  else return (f >> 1) & 7;
+}
+
+template <int T>
+__device__ __forceinline__ uint32_t tr_offset(int f, int chunk) {  // bytes
+  return (uint32_t)(f * (T * 2) + 16 * (chunk ^ tr_swz<T>(f)));
+}
+
+// Transpose an 8 (tokens) x 8 (features) bf16 block held as 8 rows of 16 bytes
+// into 8 feature rows of 8 tokens each.
+__device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
+#pragma unroll
+  for (int f = 0; f < 8; ++f) {
+    const int w = f >> 1;
+    const bool hi = f & 1;
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      uint32_t a = in[2 * p][w], b = in[2 * p + 1][w];
+      out[f][p] = hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+    }
+  }
+}
+
+// Sub-block s of a (T tokens x F features) tile -> (token chunk, feature chunk),
+// arranged so that one wave's global loads cover whole 16*F-byte rows and its
+// transposed LDS writes hit distinct banks.
+template <int F>
+__device__ __forceinline__ void subblock_coords(int s, int& tc, int& fc) {
+  constexpr int FH = F / 32;  // feature chunks / 4
+  const int rest = s >> 4;
+  fc = 4 * (rest % FH) + ((s >> 2) & 3);
+  tc = 4 * (rest / FH) + (s & 3);
+}
+
+}  // namespace sla

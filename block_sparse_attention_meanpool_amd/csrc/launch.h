@@ -1,0 +1,28 @@
+// Internal launchers (one per kernel family); the C ABI in api.cpp validates
+// arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace sla {
+
+hipError_t launch_pool(const uint16_t* q, const uint16_t* k, float* qp, float* kp, int64_t BH,
+                       int N, int d, int block, int nb, hipStream_t s);
+hipError_t launch_scores(const float* qp, const float* kp, float* S, int64_t BH, int d, int nb,
+                         float scale, hipStream_t s);
+hipError_t launch_select(const float* S, uint8_t* cls, int64_t rows, int nb, int mode, int kc,
+                         int km, float thr, hipStream_t s);
+hipError_t launch_block_mask(const uint8_t* cls, int64_t rows, int nkb, int32_t* crit_idx,
+                             int32_t* crit_cnt, int kc_max, int32_t* marg_idx, int32_t* marg_cnt,
+                             int km_max, int32_t* err_flag, hipStream_t s);
+hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
+                       int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
+                       float scale, void* o, int o_fp32, float* lse, hipStream_t s);
+hipError_t launch_linear(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
+                         int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
+                         float* o_lin, float* Hs, float* Zs, hipStream_t s);
+hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,
+                          int64_t n_elems, hipStream_t s);
+
+}  // namespace sla

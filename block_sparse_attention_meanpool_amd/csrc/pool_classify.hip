@@ -1,0 +1,244 @@
+// Mean pooling of Q and K over blocks, pooled block scores and per-row block
+// selection (SLA post: the mean-pooling step that marks blocks; NABLA post,
+// points 2-3: compressed Q/K and the 1 - thr cumulative softmax cut; Veda
+// article, "what happened": top-k over key tiles).
+#include "common.h"
+#include "launch.h"
+
+namespace sla {
+
+// ---------------------------------------------------------------------------
+// Pool: one workgroup per (tensor, batch*head, block).  256 threads; thread t
+// owns the 16-byte feature chunk t % (D/8) and walks the block's rows with a
+// stride of 256 / (D/8).  fp32 sums, reduced across row groups in LDS.
+// HBM-bound: each workgroup streams block*D*2 bytes once.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ q,
+                                                   const uint16_t* __restrict__ k,
+                                                   float* __restrict__ qp, float* __restrict__ kp,
+                                                   int N, int block, int nb) {
+  constexpr int CH = D / 8;          // 16-byte chunks per row
+  constexpr int RS = 256 / CH;       // rows per sweep
+  __shared__ float part[RS][D + 1];
+  const int blk = blockIdx.x;
+  const int64_t bh = blockIdx.y;
+  const uint16_t* src = (blockIdx.z == 0 ? q : k) + bh * (int64_t)N * D;
+  float* dst = (blockIdx.z == 0 ? qp : kp) + (bh * nb + blk) * D;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint32_t)N * D * 2);
+  const int t = threadIdx.x;
+  const int c = t % CH, r0 = t / CH;
+  const int row0 = blk * block;
+  const int valid = min(block, N - row0);
+  float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = r0; r < valid; r += RS) {
+    u32x4 x = buf_load16(rs, (uint32_t)((row0 + r) * D + c * 8) * 2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc[2 * e] += bf16_bits_to_f32(x[e] & 0xffffu);
+      acc[2 * e + 1] += bf16_bits_to_f32(x[e] >> 16);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[r0][c * 8 + e] = acc[e];
+  __syncthreads();
+  if (t < D) {
+    float s = 0.f;
+#pragma unroll 8
+    for (int r = 0; r < RS; ++r) s += part[r][t];
+    dst[t] = s / (float)valid;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Scores: S[bh][i][j] = scale * qbar_i . kbar_j in fp32.  64x64 output tile
+// per workgroup, 256 threads with 4x4 outputs each, features staged through
+// LDS in slices of 32.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qp,
+                                                    const float* __restrict__ kp,
+                                                    float* __restrict__ S, int nb, float scale) {
+  constexpr int TS = 64, KS = 32;
+  __shared__ float qs[KS][TS + 4];
+  __shared__ float ks[KS][TS + 4];
+  const int64_t bh = blockIdx.z;
+  const int i0 = blockIdx.y * TS, j0 = blockIdx.x * TS;
+  const float* qh = qp + bh * nb * D;
+  const float* kh = kp + bh * nb * D;
+  const int t = threadIdx.x;
+  const int ti = t / 16, tj = t % 16;
+  float acc[4][4] = {};
+  for (int f0 = 0; f0 < D; f0 += KS) {
+    // 64 rows x 32 features per operand = 2048 floats, 8 per thread.
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      int idx = t + 256 * e;
+      int row = idx / KS, f = idx % KS;
+      int gi = i0 + row, gj = j0 + row;
+      qs[f][row] = gi < nb ? qh[(int64_t)gi * D + f0 + f] : 0.f;
+      ks[f][row] = gj < nb ? kh[(int64_t)gj * D + f0 + f] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int f = 0; f < KS; ++f) {
+      float a[4], b[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { a[u] = qs[f][ti + 16 * u]; b[u] = ks[f][tj + 16 * u]; }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc[u][w] = fmaf(a[u], b[w], acc[u][w]);
+    }
+    __syncthreads();
+  }
+  float* Sh = S + bh * (int64_t)nb * nb;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int gi = i0 + ti + 16 * u;
+    if (gi >= nb) continue;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      int gj = j0 + tj + 16 * w;
+      if (gj < nb) Sh[(int64_t)gi * nb + gj] = scale * acc[u][w];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Select: one wave per row of S.  Each lane keeps the row's entries
+// j = lane + 64*t as 44-bit keys (order-preserving fp32 bits << 12 |
+// 4095 - j), so that a larger key means "earlier in the descending order,
+// ties to the lower j".  All keys are distinct, and a bit-by-bit search finds
+//   - the k-th largest key (top-k and the two cuts of the three-way split);
+//   - the largest key T whose prefix {key >= T} holds softmax mass >= 1 - thr
+//     (the NABLA cut), which is exactly the smallest such prefix.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint64_t order_key(float s, int j) {
+  uint32_t u = __float_as_uint(s + 0.0f);  // -0 -> +0
+  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)u << 12) | (uint64_t)(4095 - j);
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float wave_sum_f(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+__device__ __forceinline__ float wave_max_f(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+template <int MC>
+__device__ __forceinline__ uint64_t kth_largest(const uint64_t (&key)[MC], int n_here, int k) {
+  uint64_t T = 0;
+  for (int bit = 43; bit >= 0; --bit) {
+    const uint64_t cand = T | (1ull << bit);
+    int c = 0;
+#pragma unroll
+    for (int t = 0; t < MC; ++t) c += (t < n_here && key[t] >= cand) ? 1 : 0;
+    if (wave_sum_i(c) >= k) T = cand;
+  }
+  return T;
+}
+
+template <int MC>
+__global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S,
+                                                     uint8_t* __restrict__ cls, int64_t rows,
+                                                     int nb, int mode, int kc, int km, float thr) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const float* srow = S + row * nb;
+  uint8_t* crow = cls + row * nb;
+  uint64_t key[MC];
+  float sv[MC];
+  int n_here = 0;
+#pragma unroll
+  for (int t = 0; t < MC; ++t) {
+    const int j = lane + 64 * t;
+    if (j < nb) {
+      sv[t] = srow[j];
+      key[t] = order_key(sv[t], j);
+      n_here = t + 1;
+    } else {
+      sv[t] = -INFINITY;
+      key[t] = 0;
+    }
+  }
+  uint64_t t_crit, t_marg = ~0ull;
+  if (mode == 1) {  // NABLA cut
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < MC; ++t) mx = fmaxf(mx, sv[t]);
+    mx = wave_max_f(mx);
+    float e[MC];
+    float z = 0.f;
+#pragma unroll
+    for (int t = 0; t < MC; ++t) {
+      e[t] = (t < n_here && lane + 64 * t < nb) ? expf(sv[t] - mx) : 0.f;
+      z += e[t];
+    }
+    z = wave_sum_f(z);
+    const float target = (1.0f - thr) * z;
+    uint64_t T = 0;
+    for (int bit = 43; bit >= 0; --bit) {
+      const uint64_t cand = T | (1ull << bit);
+      float m = 0.f;
+#pragma unroll
+      for (int t = 0; t < MC; ++t) m += (key[t] >= cand) ? e[t] : 0.f;
+      if (wave_sum_f(m) >= target) T = cand;
+    }
+    t_crit = T;
+  } else {
+    t_crit = kth_largest<MC>(key, n_here, kc);
+    if (mode == 2 && km > 0) t_marg = kth_largest<MC>(key, n_here, kc + km);
+  }
+#pragma unroll
+  for (int t = 0; t < MC; ++t) {
+    const int j = lane + 64 * t;
+    if (j < nb) {
+      uint8_t c = 0;
+      if (key[t] >= t_crit) c = 2;
+      else if (key[t] >= t_marg) c = 1;
+      crow[j] = c;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_pool(const uint16_t* q, const uint16_t* k, float* qp, float* kp, int64_t BH,
+                       int N, int d, int block, int nb, hipStream_t s) {
+  dim3 grid(nb, (unsigned)BH, 2);
+  if (d == 128) pool_kernel<128><<<grid, 256, 0, s>>>(q, k, qp, kp, N, block, nb);
+  else pool_kernel<64><<<grid, 256, 0, s>>>(q, k, qp, kp, N, block, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_scores(const float* qp, const float* kp, float* S, int64_t BH, int d, int nb,
+                         float scale, hipStream_t s) {
+  dim3 grid((nb + 63) / 64, (nb + 63) / 64, (unsigned)BH);
+  if (d == 128) score_kernel<128><<<grid, 256, 0, s>>>(qp, kp, S, nb, scale);
+  else score_kernel<64><<<grid, 256, 0, s>>>(qp, kp, S, nb, scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_select(const float* S, uint8_t* cls, int64_t rows, int nb, int mode, int kc,
+                         int km, float thr, hipStream_t s) {
+  dim3 grid((unsigned)((rows + 3) / 4));
+  if (nb <= 256) select_kernel<4><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
+  else if (nb <= 512) select_kernel<8><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
+  else if (nb <= 1024) select_kernel<16><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
+  else if (nb <= 2048) select_kernel<32><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
+  else select_kernel<64><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
+  return hipGetLastError();
+}
+
+}  // namespace sla

@@ -1,0 +1,200 @@
+// Block-sparse softmax attention over each query block's critical key tiles
+// (SLA post: critical blocks via FlashAttention; Veda article, "what
+// happened": attention only in the selected 128-token key tiles), and the
+// dense baseline with the same core.
+//
+// One workgroup per (batch*head, query block); BLK/32 waves, each owning 32
+// query rows.  Per kept tile:
+//   K tile -> LDS row-major (rows padded by 16 bytes),
+//   V tile -> LDS transposed (feature rows, token-contiguous, XOR-swizzled),
+//   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q resident in registers,
+//   fp32 online softmax in the exp2 domain (scale * log2 e folded in),
+//   O^T += V^T P^T on the same MFMA, P taken straight from the S^T registers.
+// Computing S^T (keys x queries) puts one query per lane, so row max, row sum
+// and the O rescale are per-lane values with a single exchange between the two
+// 32-lane halves of the wave.
+#include "common.h"
+#include "launch.h"
+
+namespace sla {
+
+template <int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) void attn_fwd_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+    int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse) {
+  constexpr int NT = BLK * 2;   // threads
+  constexpr int KSTR = D + 8;   // padded K row, in bf16 elements
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * KSTR];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * BLK];
+
+  const int64_t bh = blockIdx.x / nqb;
+  const int qb = blockIdx.x % nqb;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int64_t head_off = bh * (int64_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
+
+  // Q as the B operand of S^T = K Q^T: lane holds Q[row][16 ks + 8 hf + 0..7].
+  const int qrow = qb * BLK + 32 * w + l32;
+  u32x4 qf[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = buf_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * hf) * 2);
+
+  const int count = idx ? min(cnt[bh * nqb + qb], kmax) : nkb;
+  const int32_t* list = idx ? idx + (bh * nqb + qb) * (int64_t)kmax : nullptr;
+
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int krow = swap_bits_2_3(l32);
+
+  for (int t = 0; t < count; ++t) {
+    const int j = list ? list[t] : t;
+    if (j < 0 || j >= nkb) continue;  // ignore entries outside the key-block range
+    __syncthreads();  // previous tile's LDS reads are done
+    // K tile, row-major, padded rows.
+    {
+      constexpr int CH = D / 8;
+      constexpr int PER = BLK * CH / NT;
+#pragma unroll
+      for (int e = 0; e < PER; ++e) {
+        const int c = tid + NT * e;
+        const int row = c / CH, ch = c % CH;
+        const u32x4 x = buf_load16(rk, (uint32_t)((j * BLK + row) * D + ch * 8) * 2);
+        *(u32x4*)&Ks[row * KSTR + ch * 8] = x;
+      }
+    }
+    // V tile, transposed to feature rows in 8x8 sub-blocks.
+    {
+      constexpr int NSUB = (BLK / 8) * (D / 8);
+#pragma unroll
+      for (int s0 = 0; s0 < NSUB; s0 += NT) {
+        const int s = s0 + tid;
+        if (NSUB % NT == 0 || s < NSUB) {
+          int tc, fc;
+          subblock_coords<D>(s, tc, fc);
+          u32x4 in[8], out[8];
+#pragma unroll
+          for (int r = 0; r < 8; ++r)
+            in[r] = buf_load16(rv, (uint32_t)((j * BLK + 8 * tc + r) * D + 8 * fc) * 2);
+          transpose8x8(in, out);
+#pragma unroll
+          for (int f = 0; f < 8; ++f)
+            *(u32x4*)((char*)Vt + tr_offset<BLK>(8 * fc + f, tc)) = out[f];
+        }
+      }
+    }
+    __syncthreads();
+
+    // S^T = K Q^T for this wave's 32 queries: BLK/32 blocks of 32 keys.
+    f32x16 sacc[BLK / 32];
+#pragma unroll
+    for (int kb = 0; kb < BLK / 32; ++kb) sacc[kb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+      for (int kb = 0; kb < BLK / 32; ++kb) {
+        const u32x4 a = *(const u32x4*)&Ks[(32 * kb + krow) * KSTR + 16 * ks + 8 * hf];
+        sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
+      }
+    }
+    // Keys past N in a partial last tile.
+    if ((j + 1) * BLK > N) {
+#pragma unroll
+      for (int kb = 0; kb < BLK / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = j * BLK + 32 * kb + (r < 8 ? 8 * hf + r : 16 + 8 * hf + (r - 8));
+          if (key >= N) sacc[kb][r] = -INFINITY;
+        }
+    }
+    // Online softmax (exp2 domain).
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < BLK / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const float alpha = fast_exp2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    u32x4 pb[BLK / 16];
+#pragma unroll
+    for (int kb = 0; kb < BLK / 32; ++kb)
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const float p0 = fast_exp2(fmaf(sacc[kb][8 * hs + 2 * p], sl2, -m_new));
+          const float p1 = fast_exp2(fmaf(sacc[kb][8 * hs + 2 * p + 1], sl2, -m_new));
+          const uint32_t pk = pack_bf16x2(p0, p1);
+          pb[2 * kb + hs][p] = pk;
+          l_run = add_bf16x2(pk, l_run);  // the normaliser sums the same rounded P as P V
+        }
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int ks2 = 0; ks2 < BLK / 16; ++ks2) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x4 a = *(const u32x4*)((const char*)Vt + tr_offset<BLK>(32 * db + l32, 2 * ks2 + hf));
+        oacc[db] = mfma32x32x16(a, pb[ks2], oacc[db]);
+      }
+    }
+    m_run = m_new;
+  }
+
+  const float l_tot = l_run + swap_halves(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < N) {
+    const int64_t obase = head_off + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * hf;
+        const float x0 = oacc[db][4 * g] * inv, x1 = oacc[db][4 * g + 1] * inv;
+        const float x2 = oacc[db][4 * g + 2] * inv, x3 = oacc[db][4 * g + 3] * inv;
+        if (o_fp32) {
+          *(f32x4*)((float*)o + obase + d0) = f32x4{x0, x1, x2, x3};
+        } else {
+          *(u32x2*)((uint16_t*)o + obase + d0) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        }
+      }
+    if (lse && hf == 0)
+      lse[bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, int BLK>
+static hipError_t launch_attn_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
+                                int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
+                                float scale, void* o, int o_fp32, float* lse, hipStream_t s) {
+  dim3 grid((unsigned)(BH * nb));
+  attn_fwd_kernel<D, BLK><<<grid, BLK * 2, 0, s>>>(q, k, v, N, nb, nb, idx, cnt, kmax,
+                                                    scale * kLog2e, o, o_fp32, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
+                       int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
+                       float scale, void* o, int o_fp32, float* lse, hipStream_t s) {
+  if (d == 128 && block == 128)
+    return launch_attn_t<128, 128>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, s);
+  if (d == 128 && block == 64)
+    return launch_attn_t<128, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, s);
+  if (d == 64 && block == 128)
+    return launch_attn_t<64, 128>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, s);
+  return launch_attn_t<64, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, s);
+}
+
+}  // namespace sla

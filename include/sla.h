@@ -1,0 +1,193 @@
+/*
+ * sla.h - C ABI of a gfx950 (MI355X) library for block-sparse attention with
+ * mean-pooled block selection.
+ *
+ * The method (as the pages state it):
+ *   - SLA post ("what the idea is"): attention is split into critical,
+ *     negligible and intermediate block pairs; critical pairs get softmax
+ *     attention (FlashAttention-style), negligible pairs are skipped and
+ *     intermediate (marginal) pairs get linear attention; a fast mean-pooling
+ *     step marks the blocks beforehand.
+ *   - NABLA post (points 2-4): Q and K are compressed; blocks are ranked by
+ *     the cumulative distribution of the softmax of the compressed scores and
+ *     the blocks whose summed mass reaches 1 - thr are computed.
+ *   - Veda article ("what happened"): attention is computed only over the
+ *     128-token key tiles each query needs, instead of all O(N^2) pairs.
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller, contiguous,
+ *     row-major, 16-byte aligned.  bf16 tensors are passed as uint16_t bit
+ *     patterns.  Q, K, V, O have shape [B, H, N, d].
+ *   - Shapes are int64; byte offsets may exceed 2^31.
+ *   - Supported: d in {64, 128}; block in {64, 128}; N >= 1; B, H >= 1;
+ *     nb = ceil(N / block) <= 4096.  Block j covers tokens
+ *     [j*block, min((j+1)*block, N)); a partial last block is handled
+ *     exactly (its missing tokens never enter a sum or a softmax).
+ *   - Every call validates its arguments on the host first.  On an error it
+ *     launches nothing, touches no output and returns a status < 0.
+ *   - All work is enqueued asynchronously on `stream` (0 = the null stream).
+ *     The library never allocates, frees or synchronises; it keeps no state
+ *     and may be called from several host threads.
+ *   - A HIP launch error is returned as SLA_ERR_HIP.  No C++ exception
+ *     crosses this interface.
+ *
+ * Class codes in a class map: 0 = skipped, 1 = marginal, 2 = critical.
+ */
+#ifndef SLA_H
+#define SLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sla_status;
+
+#define SLA_OK               0
+#define SLA_ERR_INVALID_ARG (-1) /* null pointer, bad size, k or thr out of range */
+#define SLA_ERR_UNSUPPORTED (-2) /* d, block or nb outside the supported set     */
+#define SLA_ERR_ALIGNMENT   (-3) /* a tensor pointer is not 16-byte aligned      */
+#define SLA_ERR_WORKSPACE   (-4) /* workspace missing or smaller than required    */
+#define SLA_ERR_HIP         (-5) /* a HIP launch failed                           */
+
+#define SLA_SEL_TOPK 0 /* keep the k_crit highest-scoring key blocks per row           */
+#define SLA_SEL_CDF  1 /* keep the smallest prefix whose pooled-softmax mass >= 1 - thr */
+#define SLA_SEL_SLA3 2 /* first k_crit critical, next k_marg marginal, rest skipped     */
+
+#define SLA_CLS_SKIP     0
+#define SLA_CLS_MARGINAL 1
+#define SLA_CLS_CRITICAL 2
+
+/* Bits set in the device error flag of sla_block_mask. */
+#define SLA_FLAG_BAD_CLASS 1 /* a class value > 2 was found (treated as skipped)   */
+#define SLA_FLAG_OVERFLOW  2 /* a row held more blocks than its list width         */
+
+/*
+ * Mean-pool Q and K over blocks, score every (query block, key block) pair
+ * and classify it.  (SLA post: the mean-pooling step that marks blocks;
+ * NABLA post points 2-3: compressed Q/K and the 1 - thr softmax-CDF cut;
+ * Veda article: top-k over key tiles.)
+ *
+ *   qbar_i = mean of the valid Q rows of block i (fp32), kbar_j likewise;
+ *   s_ij   = scale * (qbar_i . kbar_j) (fp32; scale is normally 1/sqrt(d));
+ *   each row i orders its key blocks by descending s_ij, equal scores taking
+ *   the lower j first, and then:
+ *     SLA_SEL_TOPK: the first k_crit are critical, the rest skipped;
+ *     SLA_SEL_CDF:  with p = softmax_j(s_ij), the smallest prefix whose mass
+ *                   is >= 1 - thr is critical (at least one block);
+ *     SLA_SEL_SLA3: the first k_crit are critical, the next k_marg marginal.
+ *
+ * q, k     bf16 [B, H, N, d]                                   (in)
+ * mode     SLA_SEL_*; k_crit in [1, nb] for TOPK/SLA3; k_marg in
+ *          [0, nb - k_crit] for SLA3 (ignored otherwise); thr in (0, 1) for
+ *          CDF (ignored otherwise)
+ * q_pool, k_pool  fp32 [B, H, nb, d] (out) or NULL (then kept in workspace)
+ * cls      uint8 [B, H, nb, nb] class map                       (out)
+ * ws       device workspace of at least sla_pool_classify_ws_bytes() bytes
+ */
+sla_status sla_pool_classify(const uint16_t* q, const uint16_t* k, int64_t B, int64_t H, int64_t N,
+                             int64_t d, int32_t block, int32_t mode, int32_t k_crit, int32_t k_marg,
+                             float thr, float scale, float* q_pool, float* k_pool, uint8_t* cls,
+                             void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for sla_pool_classify (pooled Q/K when not given, plus the
+ * fp32 score matrix [B, H, nb, nb]).  Returns 0 for unsupported arguments. */
+size_t sla_pool_classify_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block,
+                                  int32_t pooled_given);
+
+/*
+ * Turn a class map into compact, ascending per-row lists of key blocks: the
+ * per-query-block set of tiles each query needs (Veda article).  Works on a
+ * map from sla_pool_classify or on a caller-supplied map (mask-in).
+ *
+ * cls       uint8 [B, H, nqb, nkb]                              (in)
+ * crit_idx  int32 [B, H, nqb, kc_max]: critical key blocks in ascending
+ *           order, padded with -1                               (out)
+ * crit_cnt  int32 [B, H, nqb]                                   (out)
+ * marg_idx, marg_cnt  the same for marginal blocks, width km_max; both NULL
+ *           (and km_max 0) when no linear branch is wanted      (out)
+ * err_flag  device int32 or NULL.  A class value > 2 ORs SLA_FLAG_BAD_CLASS
+ *           into it and the pair is treated as skipped; a row with more
+ *           blocks than its width ORs SLA_FLAG_OVERFLOW, keeps its first
+ *           `width` blocks and stores count = width.  The flag is never
+ *           cleared by the library.
+ */
+sla_status sla_block_mask(const uint8_t* cls, int64_t B, int64_t H, int64_t nqb, int64_t nkb,
+                          int32_t* crit_idx, int32_t* crit_cnt, int32_t kc_max, int32_t* marg_idx,
+                          int32_t* marg_cnt, int32_t km_max, int32_t* err_flag, hipStream_t stream);
+
+/*
+ * Softmax attention over each query block's critical key blocks only (SLA
+ * post: critical blocks via FlashAttention; Veda article: attention only in
+ * the selected blocks).  For a query row n of block i:
+ *   O_s[n] = sum_m softmax_m(scale * q_n . k_m) v_m over the tokens m of the
+ *   blocks in crit_idx[i][0 .. crit_cnt[i]), renormalised over those tokens;
+ *   LSE[n] = log sum_m exp(scale * q_n . k_m) (natural log).
+ * A row with crit_cnt = 0 gets O_s = 0 and LSE = -inf.  bf16 MFMA products,
+ * fp32 online softmax and accumulation.
+ *
+ * crit_idx/crit_cnt  as written by sla_block_mask; every index in [0, nb)
+ * o_s       [B, H, N, d]; fp32 when o_is_fp32 != 0, else bf16 (RNE) (out)
+ * lse       fp32 [B, H, N] or NULL                              (out)
+ */
+sla_status sla_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                               int64_t H, int64_t N, int64_t d, int32_t block,
+                               const int32_t* crit_idx, const int32_t* crit_cnt, int32_t kc_max,
+                               float scale, void* o_s, int32_t o_is_fp32, float* lse,
+                               hipStream_t stream);
+
+/*
+ * Linear attention over each query block's marginal key blocks (SLA post:
+ * intermediate blocks via linear attention), with phi(x) = elu(x) + 1:
+ *   per key tile j: H_j = sum_t phi(k_t) v_t^T (d x d), z_j = sum_t phi(k_t);
+ *   per query block i: S_i = sum_{j in marg_i} H_j, zeta_i = sum z_j;
+ *   O_lin[n] = phi(q_n)^T S_i / (phi(q_n) . zeta_i).
+ * A row with marg_cnt = 0 gets O_lin = 0.  phi(q), phi(k) and S_i enter bf16
+ * MFMA products; sums are fp32.
+ *
+ * o_lin     fp32 [B, H, N, d]                                   (out)
+ * ws        device workspace of at least sla_linear_branch_ws_bytes() bytes
+ */
+sla_status sla_linear_branch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                                 int64_t H, int64_t N, int64_t d, int32_t block,
+                                 const int32_t* marg_idx, const int32_t* marg_cnt, int32_t km_max,
+                                 float* o_lin, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for sla_linear_branch_fwd (the per-tile states H_j, z_j). */
+size_t sla_linear_branch_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block);
+
+/*
+ * Sum the branches and round to bf16: O = bf16_rne(O_s + O_lin).  The pages
+ * only say the intermediate part goes through linear attention; the two
+ * outputs are added without weights.
+ *
+ * o_s   [n_elems], fp32 when o_s_is_fp32 != 0 else bf16         (in)
+ * o_lin fp32 [n_elems] or NULL (then O = bf16_rne(O_s))         (in)
+ * o     bf16 [n_elems]                                          (out)
+ * n_elems must be a multiple of 8.
+ */
+sla_status sla_combine(const void* o_s, int32_t o_s_is_fp32, const float* o_lin, uint16_t* o,
+                       int64_t n_elems, hipStream_t stream);
+
+/*
+ * Dense softmax attention with the same kernel core: every key block is kept
+ * for every query block.  A baseline for timing the sparse path against.
+ */
+sla_status sla_dense_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                              int64_t H, int64_t N, int64_t d, int32_t block, float scale, void* o,
+                              int32_t o_is_fp32, float* lse, hipStream_t stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* sla_status_string(sla_status status);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t sla_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLA_H */

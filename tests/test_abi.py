@@ -1,0 +1,141 @@
+"""The C ABI on the host: the library loads, exports every symbol include/sla.h
+declares, and rejects bad arguments before enqueueing anything.
+
+Argument validation runs on the host before any HIP call, so these tests need
+no GPU; no call here reaches a kernel launch.
+"""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sla.h")
+
+pytestmark = pytest.mark.skipif(
+    not os.path.exists(os.path.join(ROOT, "block_sparse_attention_meanpool_amd", "libsla.so")),
+    reason="libsla.so not built (run __graft_entry__.build())")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:sla_status|size_t|const char\*|int32_t)\s+(sla_\w+)\(",
+                                 text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def mod():
+    import block_sparse_attention_meanpool_amd as m
+    return m
+
+
+def test_header_declares_the_five_path_calls():
+    names = _declared()
+    for n in ("sla_pool_classify", "sla_block_mask", "sla_sparse_attn_fwd", "sla_linear_branch_fwd",
+              "sla_combine"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(mod):
+    so = mod.LIB_PATH
+    out = subprocess.run(["nm", "-D", "--defined-only", so], capture_output=True, text=True).stdout
+    exported = set(re.findall(r"\bT (sla_\w+)$", out, flags=re.M))
+    for n in _declared():
+        assert n in exported, n
+        assert n in mod.EXPORTS, n
+    h = ctypes.CDLL(so)
+    for n in _declared():
+        assert getattr(h, n)
+
+
+def test_status_strings_and_version(mod):
+    assert mod.sla_status_string(0) == "ok"
+    assert "aligned" in mod.sla_status_string(-3)
+    assert mod.sla_status_string(-99) == "unknown status"
+    assert mod.sla_version() >= 100
+
+
+P = ctypes.c_void_p
+GOOD = P(0x10000)        # aligned, never dereferenced: validation fails first
+ODD = P(0x10008)
+
+
+def _pc(lib, q=GOOD, k=GOOD, B=1, H=2, N=1024, d=64, block=64, mode=0, kc=4, km=0, thr=0.0,
+        scale=0.125, qp=None, kp=None, cls=GOOD, ws=GOOD, ws_bytes=1 << 40):
+    return lib.sla_pool_classify(q, k, B, H, N, d, block, mode, kc, km, thr, scale, qp, kp, cls, ws,
+                                 ws_bytes, None)
+
+
+def test_pool_classify_rejects_bad_arguments(mod):
+    lib = mod.lib()
+    assert _pc(lib, q=None) == -1
+    assert _pc(lib, N=0) == -1
+    assert _pc(lib, d=96) == -2
+    assert _pc(lib, block=32) == -2
+    assert _pc(lib, N=4096 * 64 + 1) == -2          # more than 4096 blocks
+    assert _pc(lib, q=ODD) == -3
+    assert _pc(lib, kc=0) == -1
+    assert _pc(lib, kc=17) == -1                    # nb = 16
+    assert _pc(lib, mode=2, kc=10, km=7) == -1      # k_crit + k_marg > nb
+    assert _pc(lib, mode=1, thr=0.0) == -1
+    assert _pc(lib, mode=1, thr=1.0) == -1
+    assert _pc(lib, mode=7) == -1
+    assert _pc(lib, scale=0.0) == -1
+    assert _pc(lib, qp=GOOD) == -1                  # q_pool without k_pool
+    assert _pc(lib, ws=None) == -4
+    assert _pc(lib, ws_bytes=16) == -4
+
+
+def test_workspace_sizes(mod):
+    lib = mod.lib()
+    # scores [2, 16, 16] fp32 = 2048 B, pooled 2 x [2, 16, 64] fp32 = 16384 B
+    assert lib.sla_pool_classify_ws_bytes(1, 2, 1024, 64, 64, 1) == 2048
+    assert lib.sla_pool_classify_ws_bytes(1, 2, 1024, 64, 64, 0) == 2048 + 16384
+    assert lib.sla_pool_classify_ws_bytes(1, 2, 1024, 96, 64, 0) == 0
+    # states [1, 1, 8, 128, 128] + [1, 1, 8, 128] fp32
+    assert lib.sla_linear_branch_ws_bytes(1, 1, 1000, 128, 128) == 8 * 128 * 128 * 4 + 8 * 128 * 4
+
+
+def test_other_entry_points_reject_bad_arguments(mod):
+    lib = mod.lib()
+    # block mask
+    assert lib.sla_block_mask(None, 1, 1, 4, 4, GOOD, GOOD, 2, None, None, 0, None, None) == -1
+    assert lib.sla_block_mask(GOOD, 1, 1, 4, 4, GOOD, GOOD, 0, None, None, 0, None, None) == -1
+    assert lib.sla_block_mask(GOOD, 1, 1, 4, 4, GOOD, GOOD, 5, None, None, 0, None, None) == -1
+    assert lib.sla_block_mask(GOOD, 1, 1, 4, 4, GOOD, GOOD, 2, GOOD, None, 2, None, None) == -1
+    assert lib.sla_block_mask(GOOD, 1, 1, 4, 4, GOOD, GOOD, 2, GOOD, GOOD, 0, None, None) == -1
+    # sparse attention
+    sa = lib.sla_sparse_attn_fwd
+    assert sa(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, None, GOOD, 2, 0.125, GOOD, 1, None, None) == -1
+    assert sa(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 5, 0.125, GOOD, 1, None, None) == -1
+    assert sa(GOOD, GOOD, ODD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, 0.125, GOOD, 1, None, None) == -3
+    assert sa(GOOD, GOOD, GOOD, 1, 1, 256, 80, 64, GOOD, GOOD, 2, 0.125, GOOD, 1, None, None) == -2
+    # dense baseline
+    assert lib.sla_dense_attn_fwd(GOOD, GOOD, GOOD, 1, 1, 0, 64, 64, 0.125, GOOD, 1, None, None) == -1
+    # linear branch
+    lb = lib.sla_linear_branch_fwd
+    assert lb(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, GOOD, None, 0, None) == -4
+    assert lb(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 0, GOOD, GOOD, 1 << 40, None) == -1
+    assert lb(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, ODD, GOOD, 1 << 40, None) == -3
+    # combine
+    assert lib.sla_combine(GOOD, 1, None, GOOD, 12, None) == -1
+    assert lib.sla_combine(GOOD, 1, ODD, GOOD, 16, None) == -3
+    assert lib.sla_combine(None, 1, None, GOOD, 16, None) == -1
+
+
+def test_binding_refuses_cpu_tensors(mod):
+    torch = pytest.importorskip("torch")
+    q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        mod.sla_pool_classify(q, q, 64, "topk", 1)
+
+
+def test_counts_match_the_fraction_reading(mod):
+    from fractions import Fraction as F
+    assert mod.counts_for("topk", 591, F(5, 100)) == (30, 0)
+    assert mod.counts_for("sla3", 256, F(5, 100), F(15, 100)) == (13, 39)
+    assert mod.counts_for("sla3", 1920, F(10, 100), F(5, 100)) == (192, 96)
+    assert mod.counts_for("cdf", 128) == (0, 0)
