@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import block_sparse_attention_meanpool_amd as sla
-from gpu_util import check_close, counts, f64, rne_bf16_bits, say, to_dev
+from gpu_util import LSE_MAX_ABS, REL_L2, check_close, counts, f64, rne_bf16_bits, say, to_dev
 from oracle import sla as osla
 from synth import CONFIGS, generate
 
@@ -129,7 +129,7 @@ def test_workload_parity(name):
     say(f"  oracle outputs for {len(rows)} query blocks in {time.time() - t0:.1f} s")
     cat = np.concatenate
     check_close(cat(got_s), cat(want_s), "O_s")
-    check_close(cat(got_lse), cat(want_lse), "LSE", max_abs=1e-3, rel_l2=1e-5)
+    check_close(cat(got_lse), cat(want_lse), "LSE", max_abs=LSE_MAX_ABS, rel_l2=REL_L2)
     if km:
         check_close(cat(got_lin), cat(want_lin), "O_lin")
     pre = (cat(got_s) + cat(got_lin)).astype(np.float32)

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import block_sparse_attention_meanpool_amd as sla
-from gpu_util import bits_of, check_close, f64, rne_bf16_bits, say, to_dev
+from gpu_util import LSE_MAX_ABS, REL_L2, bits_of, check_close, f64, rne_bf16_bits, say, to_dev
 from oracle import sla as osla
 from synth import generate
 from synth.configs import Spec
@@ -49,7 +49,7 @@ def test_all_kept_equals_dense(d, block, N):
     q64, k64, v64 = (osla.bf16_to_f64(x) for x in bits)
     o_ref, lse_ref, _, _ = osla.forward(q64, k64, v64, cls, block)
     check_close(o_s.cpu().numpy(), o_ref, "O_s vs dense oracle")
-    check_close(lse.cpu().numpy(), lse_ref, "LSE", max_abs=1e-3, rel_l2=1e-5)
+    check_close(lse.cpu().numpy(), lse_ref, "LSE", max_abs=LSE_MAX_ABS, rel_l2=REL_L2)
 
 
 def test_constant_v_gives_constant_output(data):
@@ -62,8 +62,11 @@ def test_constant_v_gives_constant_output(data):
     o_s, _ = sla.sla_sparse_attn_fwd(q, k, v, 128, idx, cnt, o_fp32=True)
     torch.cuda.synchronize()
     err = (o_s - float(c)).abs().max().item()
+    # numerator (MFMA accumulation of bf16(p) * c) and normaliser (sum of the
+    # same bf16(p)) differ only by fp32 accumulation order: <= c * n * 2^-23
+    n_keys = 4 * 128
     say(f"  constant V: max|O - c| = {err:.2e}")
-    assert err <= 1e-6
+    assert err <= float(c) * n_keys * 2.0 ** -23
 
 
 def test_mask_in_edge_rows_and_error_flag(data):
@@ -91,7 +94,7 @@ def test_mask_in_edge_rows_and_error_flag(data):
     check_close(o_s_np, o_s_ref, "O_s (mask-in)")
     fin = np.isfinite(lse_ref)
     assert np.array_equal(fin, np.isfinite(lse_np))
-    check_close(lse_np[fin], lse_ref[fin], "LSE (mask-in)", max_abs=1e-3, rel_l2=1e-5)
+    check_close(lse_np[fin], lse_ref[fin], "LSE (mask-in)", max_abs=LSE_MAX_ABS, rel_l2=REL_L2)
     check_close(o_lin.cpu().numpy(), o_lin_ref, "O_lin (mask-in)")
 
 
@@ -117,7 +120,16 @@ def test_list_order_does_not_matter(data):
     a, _ = sla.sla_sparse_attn_fwd(q, k, v, 128, idx, cnt, o_fp32=True)
     b, _ = sla.sla_sparse_attn_fwd(q, k, v, 128, rev, cnt, o_fp32=True)
     torch.cuda.synchronize()
-    assert (a - b).abs().max().item() < 2e-3
+    # P is rounded to bf16 relative to the running maximum, which depends on
+    # the visiting order: each weight moves by at most 2^-9 relative in either
+    # order, so the outputs differ by at most 2 * 2^-9 * max|V|
+    vmax = float(osla.bf16_to_f64(data["v"]).__abs__().max())
+    diff = (a - b).abs().max().item()
+    say(f"  order: max|a - b| = {diff:.2e} (bound {2 * 2.0 ** -9 * vmax:.2e})")
+    assert diff <= 2 * 2.0 ** -9 * vmax
+    q64, k64, v64 = (osla.bf16_to_f64(data[t]) for t in "qkv")
+    o_ref, _, _, _ = osla.forward(q64, k64, v64, cls.cpu().numpy(), 128)
+    check_close(b.cpu().numpy(), o_ref, "O_s, descending list")
 
 
 def test_forward_pipeline_matches_stages(data):
