@@ -25,7 +25,7 @@ sla_status check_shape(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block
   // one head's tensor must fit the 31-bit range of a buffer resource, with a
   // block of slack for the rows of a partial last block
   if ((N + block) * d * 2 > INT32_MAX) return SLA_ERR_UNSUPPORTED;
-  if (B * H * n > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
+  if (B * H * (n + 8) > UINT32_MAX) return SLA_ERR_UNSUPPORTED;  // grid incl. XCD padding
   *nb = n;
   return SLA_OK;
 }

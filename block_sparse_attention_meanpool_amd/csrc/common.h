@@ -24,8 +24,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16 (lo in bits 0-15), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
 // Raw buffer resource over [base, base + bytes): loads past the end return 0
@@ -43,15 +48,19 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, c
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
-// Exchange a value with the lane 32 positions away (lanes l and l^32).
-__device__ __forceinline__ float swap_halves(float x) {
+// Combine a value across the two 32-lane halves of a wave (lanes l and l^32).
+// v_permlane32_swap with one register as both operands returns
+// {[x_lo, x_lo], [x_hi, x_hi]}: every lane sees both halves' values.
+__device__ __forceinline__ float max_halves(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_halves(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // acc + lo + hi of a packed bf16 pair, in one v_dot2 against (1, 1).
 __device__ __forceinline__ float add_bf16x2(uint32_t packed, float acc) {

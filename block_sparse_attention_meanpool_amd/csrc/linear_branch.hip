@@ -181,7 +181,7 @@ __global__ __launch_bounds__(256) void lin_apply_kernel(const uint16_t* __restri
       oacc[db] = mfma32x32x16(a, pq, oacc[db]);
     }
   }
-  den += swap_halves(den);
+  den = sum_halves(den);
   const float inv = (used > 0 && den > 0.f) ? 1.f / den : 0.f;
   if (qrow < N) {
     float* orow = o_lin + head_off + (int64_t)qrow * D;

@@ -19,17 +19,24 @@
 namespace sla {
 
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
-    int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse) {
+    int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse, int seg) {
   constexpr int NT = BLK * 2;   // threads
   constexpr int KSTR = D + 8;   // padded K row, in bf16 elements
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * KSTR];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * BLK];
 
-  const int64_t bh = blockIdx.x / nqb;
-  const int qb = blockIdx.x % nqb;
+  // Workgroups go round-robin to the 8 XCDs.  XCD x takes query blocks
+  // [x*seg, (x+1)*seg) of every head, heads in order: neighbouring query
+  // blocks (which share most of their kept tiles) meet in one XCD's L2, and
+  // all XCDs work on the same head at a time.
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int64_t bh = slot / seg;
+  const int qb = xcd * seg + slot % seg;
+  if (qb >= nqb) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int64_t head_off = bh * (int64_t)N * D;
@@ -119,8 +126,8 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_kernel(
 #pragma unroll
     for (int kb = 0; kb < BLK / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, swap_halves(mx));
+      for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sacc[kb][r]), sacc[kb][r + 1]);
+    mx = max_halves(mx);
     const float m_new = fmaxf(m_run, mx * sl2);
     const float alpha = fast_exp2(m_run - m_new);
     l_run *= alpha;
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(BLK * 2) void attn_fwd_kernel(
     m_run = m_new;
   }
 
-  const float l_tot = l_run + swap_halves(l_run);
+  const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
     const int64_t obase = head_off + (int64_t)qrow * D;
@@ -179,9 +186,10 @@ template <int D, int BLK>
 static hipError_t launch_attn_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
                                 int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
                                 float scale, void* o, int o_fp32, float* lse, hipStream_t s) {
-  dim3 grid((unsigned)(BH * nb));
+  const int seg = (nb + 7) / 8;
+  dim3 grid((unsigned)(BH * seg * 8));
   attn_fwd_kernel<D, BLK><<<grid, BLK * 2, 0, s>>>(q, k, v, N, nb, nb, idx, cnt, kmax,
-                                                    scale * kLog2e, o, o_fp32, lse);
+                                                    scale * kLog2e, o, o_fp32, lse, seg);
   return hipGetLastError();
 }
 
