@@ -195,6 +195,14 @@ def main():
     stage_min = {s: float(np.min(ev[s])) for s in stages}
     log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
 
+    if args.profile:
+        # a plain 1 GiB device copy, the reference for scaling HBM counters
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     flop = kept_flop(crit_idx, crit_cnt, N, b, d) * B
     kept_frac = crit_cnt.double().mean().item() / nb
     sparse_ms = stage_ms["sparse_attn"]

@@ -84,47 +84,58 @@ __device__ __forceinline__ int swap_bits_2_3(int m) {
 }
 
 // ---------------------------------------------------------------------------
-// Transposed tile in LDS: element (row = feature f, col = token t) of a tile
-// with `T` tokens per row, stored token-contiguous in 16-byte chunks of 8
-// tokens.  Chunk c of row f lives at physical chunk c ^ swz(f), which makes
-// both the 16-lane MFMA operand reads (16 consecutive rows, one chunk) and the
-// 8x8 transpose writes below free of bank conflicts for T = 128.
+// LDS bank rules assumed below: a 16-byte-per-lane access is served 8 lanes
+// (128 bytes) at a time, or 16 lanes (256 bytes) at a time; the swizzles
+// keep every aligned group of 8 and of 16 lanes on distinct 16-byte bank
+// groups, for both the staging writes and the MFMA operand reads.
 // ---------------------------------------------------------------------------
-template <int T>
-__device__ __forceinline__ int tr_swz(int f) {
-  if constexpr (T == 128) return (f & 15) ^ ((f >> 2) & 4);
-  else return (f >> 1) & 7;
+
+// Row-major tile with CH 16-byte chunks per row: chunk ch of row r lives at
+// physical chunk ch ^ row_swz(r).  MFMA operand reads take rows
+// swap_bits_2_3(l % 32) + 32 kb, one chunk, so lanes 0..7 read rows
+// {0,1,2,3,8,9,10,11}; swapping bits 2 and 3 back makes their swizzle 0..7.
+template <int CH>
+__device__ __forceinline__ int row_swz(int r) {
+  return swap_bits_2_3(r & 15) & (CH - 1);
+}
+template <int CH>
+__device__ __forceinline__ uint32_t row_offset(int r, int chunk) {  // bytes
+  return (uint32_t)(r * (CH * 16) + 16 * (chunk ^ row_swz<CH>(r)));
 }
 
+// Transposed tile: element (row = feature f, col = token t) of a tile with T
+// tokens per row, stored token-contiguous in 16-byte chunks of 8 tokens.
+// Chunk c of row f lives at physical chunk c ^ (f % (T/8)).
 template <int T>
 __device__ __forceinline__ uint32_t tr_offset(int f, int chunk) {  // bytes
-  return (uint32_t)(f * (T * 2) + 16 * (chunk ^ tr_swz<T>(f)));
+  return (uint32_t)(f * (T * 2) + 16 * (chunk ^ (f & (T / 8 - 1))));
 }
 
 // Transpose an 8 (tokens) x 8 (features) bf16 block held as 8 rows of 16 bytes
-// into 8 feature rows of 8 tokens each.
+// into 8 feature rows of 8 tokens each (one v_perm_b32 per output dword).
 __device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
 #pragma unroll
   for (int f = 0; f < 8; ++f) {
     const int w = f >> 1;
-    const bool hi = f & 1;
+    const uint32_t sel = (f & 1) ? 0x07060302u : 0x05040100u;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      uint32_t a = in[2 * p][w], b = in[2 * p + 1][w];
-      out[f][p] = hi ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
-    }
+    for (int p = 0; p < 4; ++p)
+      out[f][p] = __builtin_amdgcn_perm(in[2 * p + 1][w], in[2 * p][w], sel);
   }
 }
 
-// Sub-block s of a (T tokens x F features) tile -> (token chunk, feature chunk),
-// arranged so that one wave's global loads cover whole 16*F-byte rows and its
-// transposed LDS writes hit distinct banks.
-template <int F>
+// Sub-block s of a (T tokens x F features) tile -> (token chunk tc, feature
+// chunk fc).  Within each 8-lane group the token chunks differ and the feature
+// chunk is shared, so each global load instruction reads 128 contiguous bytes
+// of 8 rows and the transposed LDS writes (row 8 fc + i, chunk tc) land on 8
+// (and, with the neighbouring group, 16) distinct bank groups.
+template <int T, int F>
 __device__ __forceinline__ void subblock_coords(int s, int& tc, int& fc) {
-  constexpr int FH = F / 32;  // feature chunks / 4
-  const int rest = s >> 4;
-  fc = 4 * (rest % FH) + ((s >> 2) & 3);
-  tc = 4 * (rest / FH) + (s & 3);
+  constexpr int TH = T / 64;  // groups of 8 token chunks
+  const int lane = s & 63, w = s >> 6;
+  tc = 8 * (w % TH) + (lane & 7);
+  fc = 8 * (w / TH) + (lane >> 3);
+  (void)F;
 }
 
 }  // namespace sla

@@ -5,7 +5,7 @@
 //
 // One workgroup per (batch*head, query block); BLK/32 waves, each owning 32
 // query rows.  Per kept tile:
-//   K tile -> LDS row-major (rows padded by 16 bytes),
+//   K tile -> LDS row-major, 16-byte chunks XOR-swizzled per row,
 //   V tile -> LDS transposed (feature rows, token-contiguous, XOR-swizzled),
 //   S^T = K Q^T on v_mfma_f32_32x32x16_bf16 with Q resident in registers,
 //   fp32 online softmax in the exp2 domain (scale * log2 e folded in),
@@ -24,8 +24,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
     int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse, int seg) {
   constexpr int NT = BLK * 2;   // threads
-  constexpr int KSTR = D + 8;   // padded K row, in bf16 elements
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * KSTR];
+  constexpr int CH = D / 8;     // 16-byte chunks per K row
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * BLK];
 
   // Workgroups go round-robin to the 8 XCDs.  XCD x takes query blocks
@@ -65,16 +65,15 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const int j = list ? list[t] : t;
     if (j < 0 || j >= nkb) continue;  // ignore entries outside the key-block range
     __syncthreads();  // previous tile's LDS reads are done
-    // K tile, row-major, padded rows.
+    // K tile, row-major, swizzled chunks.
     {
-      constexpr int CH = D / 8;
       constexpr int PER = BLK * CH / NT;
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
         const int c = tid + NT * e;
         const int row = c / CH, ch = c % CH;
         const u32x4 x = buf_load16(rk, (uint32_t)((j * BLK + row) * D + ch * 8) * 2);
-        *(u32x4*)&Ks[row * KSTR + ch * 8] = x;
+        *(u32x4*)((char*)Ks + row_offset<CH>(row, ch)) = x;
       }
     }
     // V tile, transposed to feature rows in 8x8 sub-blocks.
@@ -85,7 +84,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
         const int s = s0 + tid;
         if (NSUB % NT == 0 || s < NSUB) {
           int tc, fc;
-          subblock_coords<D>(s, tc, fc);
+          subblock_coords<BLK, D>(s, tc, fc);
           u32x4 in[8], out[8];
 #pragma unroll
           for (int r = 0; r < 8; ++r)
@@ -107,7 +106,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
     for (int ks = 0; ks < D / 16; ++ks) {
 #pragma unroll
       for (int kb = 0; kb < BLK / 32; ++kb) {
-        const u32x4 a = *(const u32x4*)&Ks[(32 * kb + krow) * KSTR + 16 * ks + 8 * hf];
+        const u32x4 a = *(const u32x4*)((const char*)Ks + row_offset<CH>(32 * kb + krow, 2 * ks + hf));
         sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
       }
     }
@@ -128,13 +127,21 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sacc[kb][r]), sacc[kb][r + 1]);
     mx = max_halves(mx);
-    const float m_new = fmaxf(m_run, mx * sl2);
-    const float alpha = fast_exp2(m_run - m_new);
-    l_run *= alpha;
+    // Lazy rescale: the running maximum moves only when some row's tile
+    // maximum exceeds it by more than 8 (log2 units).  P = 2^(s - m_run) then
+    // stays below 2^8, which bf16 P and the fp32 sums carry as precisely; the
+    // final division uses the same m_run, so the result is unchanged.
+    const float mt = mx * sl2;
+    if (__ballot(mt > m_run + 8.f)) {
+      const float m_new = fmaxf(m_run, mt);
+      const float alpha = fast_exp2(m_run - m_new);
+      l_run *= alpha;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+      m_run = m_new;
+    }
     u32x4 pb[BLK / 16];
 #pragma unroll
     for (int kb = 0; kb < BLK / 32; ++kb)
@@ -142,8 +149,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int hs = 0; hs < 2; ++hs)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const float p0 = fast_exp2(fmaf(sacc[kb][8 * hs + 2 * p], sl2, -m_new));
-          const float p1 = fast_exp2(fmaf(sacc[kb][8 * hs + 2 * p + 1], sl2, -m_new));
+          const float p0 = fast_exp2(fmaf(sacc[kb][8 * hs + 2 * p], sl2, -m_run));
+          const float p1 = fast_exp2(fmaf(sacc[kb][8 * hs + 2 * p + 1], sl2, -m_run));
           const uint32_t pk = pack_bf16x2(p0, p1);
           pb[2 * kb + hs][p] = pk;
           l_run = add_bf16x2(pk, l_run);  // the normaliser sums the same rounded P as P V
@@ -157,7 +164,6 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
         oacc[db] = mfma32x32x16(a, pb[ks2], oacc[db]);
       }
     }
-    m_run = m_new;
   }
 
   const float l_tot = sum_halves(l_run);
