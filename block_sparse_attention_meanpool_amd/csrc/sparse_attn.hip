@@ -188,6 +188,222 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// ---------------------------------------------------------------------------
+// d = 128, 128-token blocks: the same computation, pipelined.  Each kept tile
+// is processed as two 64-key halves streamed through double-buffered LDS by
+// asynchronous LDS-direct buffer loads: the loads of half u+1 are issued
+// before half u is computed, so their latency hides behind its MFMA and
+// softmax work, with one barrier per half.  64 KB of LDS and <= 256 VGPRs keep
+// two workgroups per CU.  V stays row-major in LDS and reaches the MFMA as
+// V^T through ds_read_b64_tr_b16: within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte chunks addressed by lanes 4e + i / 4 (e = 0..3),
+// so two such reads give a lane 8 consecutive keys of its own feature column.
+// ---------------------------------------------------------------------------
+namespace pipe {
+
+constexpr int D = 128, BLK = 128, HALF = 64, NT = 256;
+constexpr int ROWB = D * 2;              // bytes per K / V row
+constexpr int BUFB = HALF * ROWB;        // 16 KB per half tile
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+// V rows: chunk c of row r at physical chunk c ^ v_swz(r).  A transpose read
+// touches rows 4a..4a+3 and two (16 lanes) or four (32 lanes) adjacent
+// chunks; the table keeps those on distinct bank groups in both cases.
+__device__ __forceinline__ int v_swz(int r) { return (0xAC60 >> (4 * (r & 3))) & 15; }
+
+__device__ __forceinline__ void wait_vm0() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt untouched
+}
+
+struct Ctx {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  int N, nkb, lane, w;
+};
+
+// Issue the asynchronous loads of half hh of key tile j into (kbuf, vbuf).
+// Each wave moves 4 KB of K and 4 KB of V: 4 instructions of 64 lanes x 16 B,
+// lane-contiguous in LDS; the global chunk each lane fetches implements the
+// swizzle.  Rows past N are clamped to N - 1 (finite data, masked in S).
+__device__ __forceinline__ void issue_half(const Ctx& c, int j, int hh, char* kbuf, char* vbuf) {
+  const int jj = min(max(j, 0), c.nkb - 1);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int inst = 4 * c.w + e;                  // 1 KB LDS block, 4 rows
+    const int row = 4 * inst + (c.lane >> 4);      // row within the half tile
+    const int grow = min(jj * BLK + HALF * hh + row, c.N - 1);
+    const int kch = (c.lane & 15) ^ row_swz<16>(row);
+    const int vch = (c.lane & 15) ^ v_swz(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rk, (lds_void_ptr)(kbuf + inst * 1024), 16,
+                                             (uint32_t)(grow * D + kch * 8) * 2, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rv, (lds_void_ptr)(vbuf + inst * 1024), 16,
+                                             (uint32_t)(grow * D + vch * 8) * 2, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ u32x2 tr_read(const char* vbuf, int row, int d0) {
+  const int chunk = d0 >> 3;
+  const uint32_t off = (uint32_t)(row * ROWB + 16 * (chunk ^ v_swz(row)) + 8 * ((d0 >> 2) & 1));
+  typedef __attribute__((address_space(3))) s16x4* lptr;
+  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(vbuf + off));
+  return __builtin_bit_cast(u32x2, x);
+}
+
+// One 64-key half: S^T = K Q^T, masking, online softmax, O^T += V^T P^T.
+__device__ __forceinline__ void compute_half(const char* kbuf, const char* vbuf, const u32x4 (&qf)[8],
+                                             f32x16 (&oacc)[4], float& m_run, float& l_run,
+                                             int key0, int N, float sl2, int l32, int hf, int krow,
+                                             int lane) {
+  f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const u32x4 a = *(const u32x4*)(kbuf + row_offset<16>(32 * kb + krow, 2 * ks + hf));
+      sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
+    }
+  }
+  if (key0 + HALF > N) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = key0 + 32 * kb + (r < 8 ? 8 * hf + r : 16 + 8 * hf + (r - 8));
+        if (key >= N) sacc[kb][r] = -INFINITY;
+      }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, sacc[kb][r]), sacc[kb][r + 1]);
+  mx = max_halves(mx);
+  const float mt = mx * sl2;
+  if (__ballot(mt > m_run + 8.f)) {  // lazy rescale, as in the generic kernel
+    const float m_new = fmaxf(m_run, mt);
+    const float alpha = fast_exp2(m_run - m_new);
+    l_run *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+    m_run = m_new;
+  }
+  u32x4 pb[4];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float p0 = fast_exp2(fmaf(sacc[kb][8 * hs + 2 * p], sl2, -m_run));
+        const float p1 = fast_exp2(fmaf(sacc[kb][8 * hs + 2 * p + 1], sl2, -m_run));
+        const uint32_t pk = pack_bf16x2(p0, p1);
+        pb[2 * kb + hs][p] = pk;
+        l_run = add_bf16x2(pk, l_run);
+      }
+  const int g = lane >> 4, sl = lane & 15;
+#pragma unroll
+  for (int ks2 = 0; ks2 < 4; ++ks2) {
+    const int rbase = 16 * ks2 + 8 * (g >> 1) + (sl >> 2);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int d0 = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
+      const u32x2 lo = tr_read(vbuf, rbase, d0);
+      const u32x2 hi = tr_read(vbuf, rbase + 4, d0);
+      oacc[db] = mfma32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[ks2], oacc[db]);
+    }
+  }
+  (void)l32;
+}
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pipe_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
+    int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
+    int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse, int seg) {
+  __shared__ __attribute__((aligned(1024))) char K0[BUFB];
+  __shared__ __attribute__((aligned(1024))) char V0[BUFB];
+  __shared__ __attribute__((aligned(1024))) char K1[BUFB];
+  __shared__ __attribute__((aligned(1024))) char V1[BUFB];
+
+  const int xcd = blockIdx.x & 7;
+  const int slot = blockIdx.x >> 3;
+  const int64_t bh = slot / seg;
+  const int qb = xcd * seg + slot % seg;
+  if (qb >= nqb) return;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int64_t head_off = bh * (int64_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  Ctx c;
+  c.rk = make_rsrc(k + head_off, head_bytes);
+  c.rv = make_rsrc(v + head_off, head_bytes);
+  c.N = N;
+  c.nkb = nkb;
+  c.lane = lane;
+  c.w = w;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
+
+  const int count = idx ? min(cnt[bh * nqb + qb], kmax) : nkb;
+  const int32_t* list = idx ? idx + (bh * nqb + qb) * (int64_t)kmax : nullptr;
+
+  int j_cur = count > 0 ? (list ? list[0] : 0) : 0;
+  if (count > 0) issue_half(c, j_cur, 0, K0, V0);
+
+  const int qrow = qb * BLK + 32 * w + l32;
+  u32x4 qf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    qf[ks] = buf_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * hf) * 2);
+
+  f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  float m_run = -INFINITY, l_run = 0.f;
+  const int krow = swap_bits_2_3(l32);
+
+  for (int t = 0; t < count; ++t) {
+    const bool ok = j_cur >= 0 && j_cur < nkb;
+    // next tile index: loaded before the wait below, which drains it together
+    // with the loads of buffer 0
+    const int j_next = (t + 1 < count) ? (list ? list[t + 1] : t + 1) : 0;
+    // first half of tile j_cur, in buffer 0
+    wait_vm0();
+    __syncthreads();  // buffer 0 complete; every wave is done with buffer 1
+    issue_half(c, j_cur, 1, K1, V1);
+    if (ok) compute_half(K0, V0, qf, oacc, m_run, l_run, j_cur * BLK, N, sl2, l32, hf, krow, lane);
+    // second half, in buffer 1
+    wait_vm0();
+    __syncthreads();  // buffer 1 complete; every wave is done with buffer 0
+    if (t + 1 < count) issue_half(c, j_next, 0, K0, V0);
+    if (ok && j_cur * BLK + HALF < N)
+      compute_half(K1, V1, qf, oacc, m_run, l_run, j_cur * BLK + HALF, N, sl2, l32, hf, krow, lane);
+    j_cur = j_next;
+  }
+
+  const float l_tot = sum_halves(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < N) {
+    const int64_t obase = head_off + (int64_t)qrow * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = 32 * db + 8 * g + 4 * hf;
+        const float x0 = oacc[db][4 * g] * inv, x1 = oacc[db][4 * g + 1] * inv;
+        const float x2 = oacc[db][4 * g + 2] * inv, x3 = oacc[db][4 * g + 3] * inv;
+        if (o_fp32) {
+          *(f32x4*)((float*)o + obase + d0) = f32x4{x0, x1, x2, x3};
+        } else {
+          *(u32x2*)((uint16_t*)o + obase + d0) = u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+        }
+      }
+    if (lse && hf == 0)
+      lse[bh * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace pipe
+
 template <int D, int BLK>
 static hipError_t launch_attn_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
                                 int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
@@ -202,8 +418,12 @@ static hipError_t launch_attn_t(const uint16_t* q, const uint16_t* k, const uint
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                        int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
                        float scale, void* o, int o_fp32, float* lse, hipStream_t s) {
-  if (d == 128 && block == 128)
-    return launch_attn_t<128, 128>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, s);
+  if (d == 128 && block == 128) {
+    const int seg = (nb + 7) / 8;
+    pipe::attn_fwd_pipe_kernel<<<dim3((unsigned)(BH * seg * 8)), pipe::NT, 0, s>>>(
+        q, k, v, N, nb, nb, idx, cnt, kmax, scale * kLog2e, o, o_fp32, lse, seg);
+    return hipGetLastError();
+  }
   if (d == 128 && block == 64)
     return launch_attn_t<128, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, s);
   if (d == 64 && block == 128)
