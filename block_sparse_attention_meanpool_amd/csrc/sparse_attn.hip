@@ -112,13 +112,13 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     // Keys past N in a partial last tile.
     if ((j + 1) * BLK > N) {
+      // register r of block kb holds key j BLK + 8 hf + (32 kb + r + 8 [r >= 8])
+      const int lim = N - j * BLK - 8 * hf;
 #pragma unroll
       for (int kb = 0; kb < BLK / 32; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = j * BLK + 32 * kb + (r < 8 ? 8 * hf + r : 16 + 8 * hf + (r - 8));
-          if (key >= N) sacc[kb][r] = -INFINITY;
-        }
+        for (int r = 0; r < 16; ++r)
+          if (32 * kb + r + (r >= 8 ? 8 : 0) >= lim) sacc[kb][r] = -INFINITY;
     }
     // Online softmax (exp2 domain).
     float mx = -INFINITY;
@@ -265,13 +265,13 @@ __device__ __forceinline__ void compute_half(const char* kbuf, const char* vbuf,
     }
   }
   if (key0 + HALF > N) {
+    // register r of block kb holds key key0 + 8 hf + (32 kb + r + 8 [r >= 8])
+    const int lim = N - key0 - 8 * hf;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = key0 + 32 * kb + (r < 8 ? 8 * hf + r : 16 + 8 * hf + (r - 8));
-        if (key >= N) sacc[kb][r] = -INFINITY;
-      }
+      for (int r = 0; r < 16; ++r)
+        if (32 * kb + r + (r >= 8 ? 8 : 0) >= lim) sacc[kb][r] = -INFINITY;
   }
   float mx = -INFINITY;
 #pragma unroll
