@@ -142,9 +142,7 @@ sla_status sla_dense_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16
 size_t sla_linear_branch_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {
   int64_t nb = 0;
   if (check_shape(B, H, N, d, block, &nb) != SLA_OK) return 0;
-  const int64_t BH = B * H;
-  return round_up((size_t)(BH * nb * d * d) * sizeof(float), 256) +
-         round_up((size_t)(BH * nb * d) * sizeof(float), 256);
+  return sla::linear_ws_layout(B * H, (int)nb, (int)d).total;
 }
 
 sla_status sla_linear_branch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
@@ -159,12 +157,8 @@ sla_status sla_linear_branch_fwd(const uint16_t* q, const uint16_t* k, const uin
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_lin)) return SLA_ERR_ALIGNMENT;
   const size_t need = sla_linear_branch_ws_bytes(B, H, N, d, block);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
-  const int64_t BH = B * H;
-  float* Hs = static_cast<float*>(ws);
-  float* Zs = reinterpret_cast<float*>(static_cast<char*>(ws) +
-                                       round_up((size_t)(BH * nb * d * d) * sizeof(float), 256));
-  return from_hip(sla::launch_linear(q, k, v, BH, (int)N, (int)d, block, (int)nb, marg_idx,
-                                     marg_cnt, km_max, o_lin, Hs, Zs, stream));
+  return from_hip(sla::launch_linear(q, k, v, B * H, (int)N, (int)d, block, (int)nb, marg_idx,
+                                     marg_cnt, km_max, o_lin, ws, stream));
 }
 
 sla_status sla_combine(const void* o_s, int32_t o_s_is_fp32, const float* o_lin, uint16_t* o,

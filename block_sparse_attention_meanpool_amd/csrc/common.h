@@ -138,4 +138,45 @@ __device__ __forceinline__ void subblock_coords(int s, int& tc, int& fc) {
   (void)F;
 }
 
+
+// ---------------------------------------------------------------------------
+// Row-major bf16 tiles of 256-byte rows (128 elements) read as transposed MFMA
+// operands with ds_read_b64_tr_b16.  Within each 16-lane group, lane i of the
+// instruction receives element i % 4 of the 8-byte chunks addressed by lanes
+// 4e + i / 4 (e = 0..3).  Pointing lane s of group g at row 4a + s / 4 and
+// columns c0 + 16 (g & 1) + 4 (s & 3) .. +3 therefore hands lane g*16 + s the
+// four values of column c0 + 16 (g & 1) + s in rows 4a .. 4a+3; two reads give
+// 8 consecutive rows of one column, i.e. one K-contiguous MFMA operand.
+// Chunk c of row r is stored at physical chunk c ^ trs_swz(r): a transpose
+// read touches rows 4a..4a+3 and two (16 lanes) or four (32 lanes) adjacent
+// chunks, and the table keeps those on distinct bank groups in both cases.
+// ---------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
+
+__device__ __forceinline__ int trs_swz(int r) { return (0xAC60 >> (4 * (r & 3))) & 15; }
+
+__device__ __forceinline__ u32x2 tr_read256(const char* base, int row, int col) {
+  const int chunk = col >> 3;
+  const uint32_t off = (uint32_t)(row * 256 + 16 * (chunk ^ trs_swz(row)) + 8 * ((col >> 2) & 1));
+  typedef __attribute__((address_space(3))) s16x4* lptr;
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(base + off)));
+}
+
+// K-contiguous MFMA A operand for MFMA row (lane % 32) of the 32-column block
+// starting at col0, rows k0 + 8 (lane / 32) + 0..7 of a swizzled 256-byte-row
+// tile (see tr_read256).
+__device__ __forceinline__ u32x4 tr_operand(const char* base, int k0, int col0, int lane) {
+  const int g = lane >> 4, s = lane & 15;
+  const int row = k0 + 8 * (g >> 1) + (s >> 2);
+  const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
+  const u32x2 lo = tr_read256(base, row, col);
+  const u32x2 hi = tr_read256(base, row + 4, col);
+  return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+__device__ __forceinline__ void wait_vmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt untouched
+}
+
 }  // namespace sla

@@ -19,9 +19,17 @@ hipError_t launch_block_mask(const uint8_t* cls, int64_t rows, int nkb, int32_t*
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                        int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
                        float scale, void* o, int o_fp32, float* lse, hipStream_t s);
+// Linear-branch workspace: per-tile states H_j^T (bf16) and z_j (fp32), the
+// marginal bit matrix (words 32-bit words per query block) and the gathered
+// S_i^T (bf16), each piece 256-byte aligned.
+struct LinearWs {
+  int words;
+  size_t ht_bytes, z_bytes, bits_bytes, c_bytes, total;
+};
+LinearWs linear_ws_layout(int64_t BH, int nb, int d);
 hipError_t launch_linear(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                          int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
-                         float* o_lin, float* Hs, float* Zs, hipStream_t s);
+                         float* o_lin, void* ws, hipStream_t s);
 hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,
                           int64_t n_elems, hipStream_t s);
 

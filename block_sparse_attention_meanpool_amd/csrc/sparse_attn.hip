@@ -205,17 +205,9 @@ constexpr int D = 128, BLK = 128, HALF = 64, NT = 256;
 constexpr int ROWB = D * 2;              // bytes per K / V row
 constexpr int BUFB = HALF * ROWB;        // 16 KB per half tile
 
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_void_ptr;
+__device__ __forceinline__ int v_swz(int r) { return trs_swz(r); }
 
-// V rows: chunk c of row r at physical chunk c ^ v_swz(r).  A transpose read
-// touches rows 4a..4a+3 and two (16 lanes) or four (32 lanes) adjacent
-// chunks; the table keeps those on distinct bank groups in both cases.
-__device__ __forceinline__ int v_swz(int r) { return (0xAC60 >> (4 * (r & 3))) & 15; }
-
-__device__ __forceinline__ void wait_vm0() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0); expcnt and lgkmcnt untouched
-}
+__device__ __forceinline__ void wait_vm0() { wait_vmcnt0(); }
 
 struct Ctx {
   __amdgpu_buffer_rsrc_t rk, rv;
@@ -240,14 +232,6 @@ __device__ __forceinline__ void issue_half(const Ctx& c, int j, int hh, char* kb
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rv, (lds_void_ptr)(vbuf + inst * 1024), 16,
                                              (uint32_t)(grow * D + vch * 8) * 2, 0, 0, 0);
   }
-}
-
-__device__ __forceinline__ u32x2 tr_read(const char* vbuf, int row, int d0) {
-  const int chunk = d0 >> 3;
-  const uint32_t off = (uint32_t)(row * ROWB + 16 * (chunk ^ v_swz(row)) + 8 * ((d0 >> 2) & 1));
-  typedef __attribute__((address_space(3))) s16x4* lptr;
-  const s16x4 x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(vbuf + off));
-  return __builtin_bit_cast(u32x2, x);
 }
 
 // One 64-key half: S^T = K Q^T, masking, online softmax, O^T += V^T P^T.
@@ -303,17 +287,11 @@ __device__ __forceinline__ void compute_half(const char* kbuf, const char* vbuf,
         pb[2 * kb + hs][p] = pk;
         l_run = add_bf16x2(pk, l_run);
       }
-  const int g = lane >> 4, sl = lane & 15;
 #pragma unroll
   for (int ks2 = 0; ks2 < 4; ++ks2) {
-    const int rbase = 16 * ks2 + 8 * (g >> 1) + (sl >> 2);
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int d0 = 32 * db + 16 * (g & 1) + 4 * (sl & 3);
-      const u32x2 lo = tr_read(vbuf, rbase, d0);
-      const u32x2 hi = tr_read(vbuf, rbase + 4, d0);
-      oacc[db] = mfma32x32x16(u32x4{lo[0], lo[1], hi[0], hi[1]}, pb[ks2], oacc[db]);
-    }
+    for (int db = 0; db < 4; ++db)
+      oacc[db] = mfma32x32x16(tr_operand(vbuf, 16 * ks2, 32 * db, lane), pb[ks2], oacc[db]);
   }
   (void)l32;
 }

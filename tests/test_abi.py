@@ -95,8 +95,10 @@ def test_workspace_sizes(mod):
     assert lib.sla_pool_classify_ws_bytes(1, 2, 1024, 64, 64, 1) == 2048
     assert lib.sla_pool_classify_ws_bytes(1, 2, 1024, 64, 64, 0) == 2048 + 16384
     assert lib.sla_pool_classify_ws_bytes(1, 2, 1024, 96, 64, 0) == 0
-    # states [1, 1, 8, 128, 128] + [1, 1, 8, 128] fp32
-    assert lib.sla_linear_branch_ws_bytes(1, 1, 1000, 128, 128) == 8 * 128 * 128 * 4 + 8 * 128 * 4
+    # bf16 states H_j^T [8, 128*128], fp32 z_j [8, 128], bit rows [8, 2 words] (256-byte
+    # aligned), bf16 gathered S_i^T [8, 128*128]
+    assert lib.sla_linear_branch_ws_bytes(1, 1, 1000, 128, 128) == \
+        8 * 128 * 128 * 2 + 8 * 128 * 4 + 256 + 8 * 128 * 128 * 2
 
 
 def test_other_entry_points_reject_bad_arguments(mod):
