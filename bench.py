@@ -6,20 +6,25 @@ the seeded generator (already resident in HBM when timing starts).
 
 A step is one pass of the whole path: pool + classify, list compaction,
 sparse attention (bf16 output written directly: this workload has no
-marginal tiles, so the linear branch and the sum are empty).
+marginal tiles, so the linear branch and the sum are empty).  Workloads
+with marginal tiles (--config wan1p3b, long_clip_95, long_clip_90) run the
+linear branch's preparation and then the fused sparse + linear kernel that
+stores O once; --unfused times the separate sparse, linear and combine calls.
 
 Printed JSON line:
   value        kept-block attention FLOP per step / step time (TFLOP/s),
                i.e. whole-layer effective throughput;
   roofline     the sparse-attention kernel alone: kept FLOP per launch /
                its average launch time (HIP events on its stream) against
-               the bf16 dense MFMA peak;
+               the bf16 dense MFMA peak; traffic = HBM bytes per launch from
+               the committed counter summary of the same kernel source, else
+               null;
   cpu_baseline the fp64 oracle on the host cores on a bounded sample;
   extra        per-stage times, dense baselines (this library's dense kernel
                and torch SDPA) and ms/layer ratios.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--config wan14b]
-                [--no-cpu-baseline] [--no-dense] [--profile]
+                [--no-cpu-baseline] [--no-dense] [--profile] [--unfused]
 """
 
 import argparse
@@ -56,6 +61,56 @@ def kept_flop(crit_idx, crit_cnt, N, block, d):
     per = (keys.sum(-1) * rows).sum().item()
     del nb
     return 4.0 * per * d
+
+
+# Sources of the sparse-attention kernel; a counter summary applies only to the
+# build whose sources hash to the value recorded in it.
+KERNEL_SOURCES = ["sparse_attn.hip", "common.h", "linear_apply.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_meanpool_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(config_name):
+    """HBM bytes per launch of the sparse-attention kernel from the committed
+    counter summary (FETCH_SIZE + WRITE_SIZE, copy-calibrated), or None when
+    there is none for this workload or the kernel has changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_attn_{config_name}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                key, val = line[2:].split(": ", 1)
+                fields[key.strip()] = val.strip().strip("`")
+    if fields.get("kernel source sha256") != kernel_source_hash():
+        return None
+    try:
+        return {"fetch": float(fields["fetch bytes per launch"]),
+                "write": float(fields["write bytes per launch"])}
+    except (KeyError, ValueError):
+        return None
+
+
+def describe(spec, kc, km):
+    grid = f" ({'x'.join(str(x) for x in spec.grid)})" if spec.grid else ""
+    if spec.mode == "topk":
+        sel = (f"top-{kc} of {spec.nb} key tiles per query block "
+               f"({100 * (1 - kc / spec.nb):.0f}% sparsity)")
+    elif spec.mode == "cdf":
+        sel = f"softmax-CDF cut at thr={spec.thr}"
+    else:
+        sel = (f"{kc} critical + {km} marginal (linear) of {spec.nb} key tiles per query block"
+               + (" (mask given)" if spec.mode == "maskin" else ""))
+    return (f"{spec.name}: B={spec.B} H={spec.H} N={spec.N}{grid} d={spec.d} "
+            f"block={spec.block}, {sel}")
 
 
 def cpu_baseline(spec, data, kc, km, budget_s=20.0):
@@ -103,6 +158,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for a profiler")
+    ap.add_argument("--unfused", action="store_true",
+                    help="with a linear branch: separate sparse, linear and combine calls")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path shards by "
@@ -140,14 +197,19 @@ def main():
     if km:
         marg_idx = torch.empty((B, H, nb, km), dtype=torch.int32, device=dev)
         marg_cnt = torch.empty((B, H, nb), dtype=torch.int32, device=dev)
-        o_s = torch.empty(q.shape, dtype=torch.float32, device=dev)
-        o_lin = torch.empty(q.shape, dtype=torch.float32, device=dev)
+        if args.unfused:
+            o_s = torch.empty(q.shape, dtype=torch.float32, device=dev)
+            o_lin = torch.empty(q.shape, dtype=torch.float32, device=dev)
         lin_ws = torch.empty(sla.lib().sla_linear_branch_ws_bytes(B, H, N, d, b), dtype=torch.uint8,
                              device=dev)
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
-    stages = ["pool_classify", "block_mask", "sparse_attn"] + (["linear_branch", "combine"] if km else [])
+    fused = bool(km) and not args.unfused
+    if fused:
+        stages = ["pool_classify", "block_mask", "linear_prepare", "sparse_attn"]
+    else:
+        stages = ["pool_classify", "block_mask", "sparse_attn"] + (["linear_branch", "combine"] if km else [])
     ev = {s: [] for s in stages}
 
     def step(record):
@@ -160,7 +222,14 @@ def main():
         sla.sla_block_mask(cls, kc_max, km, crit_idx, crit_cnt, marg_idx, marg_cnt)
         if record:
             marks[2].record(stream)
-        if km:
+        if fused:
+            sla.sla_linear_branch_prepare(k, v, b, marg_idx, marg_cnt, ws=lin_ws)
+            if record:
+                marks[3].record(stream)
+            sla.sla_sparse_linear_attn_fwd(q, k, v, b, crit_idx, crit_cnt, lin_ws, o=o)
+            if record:
+                marks[4].record(stream)
+        elif km:
             sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt, o_s=o_s)
             if record:
                 marks[3].record(stream)
@@ -253,16 +322,21 @@ def main():
         extra["speedup_vs_best_dense"] = best_dense / ms_step
         log(f"[bench] dense: ours {extra['dense_kernel_ms']:.2f} ms, sdpa {extra.get('torch_sdpa_ms')}")
 
+    traffic = measured_traffic(spec.name)
+    if traffic is not None:
+        extra["attn_hbm_bytes_per_launch"] = traffic
+        extra["attn_hbm_gbs"] = (traffic["fetch"] + traffic["write"]) / (sparse_ms * 1e-3) / 1e9
     result = {
         "metric": "effective attn TFLOP/s on kept blocks; ms/layer vs dense at 95% sparsity",
         "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic (seeded random-Fourier video-latent fields + noise)",
-        "config": {"workload": f"{spec.name}: B={B} H={H} N={N} (21x45x80) d={d} block={b}, "
-                               f"top-{kc} of {nb} key tiles per query block (95% sparsity)",
-                   "global_batch": B, "seq_len": N, "parallelism": "none (1 GPU)"},
+        "config": {"workload": describe(spec, kc, km), "global_batch": B, "seq_len": N,
+                   "parallelism": "none (1 GPU)",
+                   "path": "fused" if fused else ("unfused" if km else "sparse only")},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None},
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None if traffic is None else traffic["fetch"] + traffic["write"]},
         "extra": extra,
     }
     if not args.no_cpu_baseline:

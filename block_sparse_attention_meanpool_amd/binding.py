@@ -40,6 +40,10 @@ _SIGS = {
     "sla_linear_branch_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _P,
                                      _P, _SZ, _P]),
     "sla_linear_branch_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32]),
+    "sla_linear_branch_prepare": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _P,
+                                         _SZ, _P]),
+    "sla_sparse_linear_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32,
+                                          _F, _P, _SZ, _P, _I32, _P, _P]),
     "sla_combine": (_I32, [_P, _I32, _P, _P, _I64, _P]),
     "sla_dense_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _F, _P, _I32, _P, _P]),
     "sla_status_string": (ctypes.c_char_p, [_I32]),
@@ -215,6 +219,41 @@ def sla_linear_branch_fwd(q, k, v, block, marg_idx, marg_cnt, o_lin=None, ws=Non
     return o_lin
 
 
+def sla_linear_branch_prepare(k, v, block, marg_idx, marg_cnt, ws=None, stream=None):
+    for t, n in ((k, "k"), (v, "v")):
+        _dev(t, torch.bfloat16, n)
+    _dev(marg_idx, torch.int32, "marg_idx")
+    _dev(marg_cnt, torch.int32, "marg_cnt")
+    B, H, N, d = k.shape
+    need = lib().sla_linear_branch_ws_bytes(B, H, N, d, block)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
+    _call("sla_linear_branch_prepare", _ptr(k), _ptr(v), B, H, N, d, block, _ptr(marg_idx),
+          _ptr(marg_cnt), marg_idx.shape[-1], _ptr(ws), ws.numel() * ws.element_size(),
+          _stream(stream))
+    return ws
+
+
+def sla_sparse_linear_attn_fwd(q, k, v, block, crit_idx, crit_cnt, lin_ws, scale=None, o=None,
+                               o_fp32=False, lse=None, want_lse=False, stream=None):
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _dev(t, torch.bfloat16, n)
+    _dev(crit_idx, torch.int32, "crit_idx")
+    _dev(crit_cnt, torch.int32, "crit_cnt")
+    _dev(lin_ws, torch.uint8, "lin_ws")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if o is None:
+        o = torch.empty(q.shape, dtype=torch.float32 if o_fp32 else torch.bfloat16, device=q.device)
+    if want_lse and lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _call("sla_sparse_linear_attn_fwd", _ptr(q), _ptr(k), _ptr(v), B, H, N, d, block,
+          _ptr(crit_idx), _ptr(crit_cnt), crit_idx.shape[-1], float(scale), _ptr(lin_ws),
+          lin_ws.numel(), _ptr(o), int(o.dtype == torch.float32), _ptr(lse), _stream(stream))
+    return o, lse
+
+
 def sla_combine(o_s, o_lin=None, o=None, stream=None):
     if o is None:
         o = torch.empty(o_s.shape, dtype=torch.bfloat16, device=o_s.device)
@@ -228,9 +267,11 @@ def sla_combine(o_s, o_lin=None, o=None, stream=None):
 # ---------------------------------------------------------------------------
 
 def forward(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=None, o_fp32=False,
-            stream=None):
+            fused=False, stream=None):
     """Pool and classify (unless `cls` is given: mask-in), compact the lists,
-    run the sparse and linear branches and combine.
+    run the sparse and linear branches and combine.  With fused=True and a
+    linear branch, the two branches run as sla_linear_branch_prepare plus
+    sla_sparse_linear_attn_fwd (no O_s / O_lin intermediates).
 
     mode "topk" (keep), "cdf" (thr), "sla3" (keep, marg).  With a given cls,
     `keep`/`marg` only size the lists (default: the whole row).
@@ -249,7 +290,11 @@ def forward(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=Non
     crit_idx, crit_cnt, marg_idx, marg_cnt = sla_block_mask(cls, kc_max, km_max, stream=stream)
     out = {"cls": cls, "crit_idx": crit_idx, "crit_cnt": crit_cnt, "marg_idx": marg_idx,
            "marg_cnt": marg_cnt}
-    if km_max:
+    if km_max and fused:
+        lin_ws = sla_linear_branch_prepare(k, v, block, marg_idx, marg_cnt, stream=stream)
+        o, _ = sla_sparse_linear_attn_fwd(q, k, v, block, crit_idx, crit_cnt, lin_ws, stream=stream)
+        out.update(o=o)
+    elif km_max:
         o_s, _ = sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, o_fp32=True, stream=stream)
         o_lin = sla_linear_branch_fwd(q, k, v, block, marg_idx, marg_cnt, stream=stream)
         o = sla_combine(o_s, o_lin, stream=stream)

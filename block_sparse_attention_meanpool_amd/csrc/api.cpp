@@ -123,7 +123,8 @@ sla_status sla_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
   if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_s)) return SLA_ERR_ALIGNMENT;
   return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
-                                   crit_cnt, kc_max, scale, o_s, o_is_fp32 != 0, lse, stream));
+                                   crit_cnt, kc_max, scale, o_s, o_is_fp32 != 0, lse, nullptr,
+                                   stream));
 }
 
 sla_status sla_dense_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
@@ -136,13 +137,29 @@ sla_status sla_dense_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16
   if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SLA_ERR_ALIGNMENT;
   return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, nullptr, nullptr,
-                                   (int)nb, scale, o, o_is_fp32 != 0, lse, stream));
+                                   (int)nb, scale, o, o_is_fp32 != 0, lse, nullptr, stream));
 }
 
 size_t sla_linear_branch_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {
   int64_t nb = 0;
   if (check_shape(B, H, N, d, block, &nb) != SLA_OK) return 0;
   return sla::linear_ws_layout(B * H, (int)nb, (int)d).total;
+}
+
+sla_status sla_linear_branch_prepare(const uint16_t* k, const uint16_t* v, int64_t B, int64_t H,
+                                     int64_t N, int64_t d, int32_t block, const int32_t* marg_idx,
+                                     const int32_t* marg_cnt, int32_t km_max, void* ws,
+                                     size_t ws_bytes, hipStream_t stream) {
+  int64_t nb = 0;
+  sla_status st = check_shape(B, H, N, d, block, &nb);
+  if (st != SLA_OK) return st;
+  if (!k || !v || !marg_idx || !marg_cnt) return SLA_ERR_INVALID_ARG;
+  if (km_max < 1 || km_max > nb) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(k) || !aligned16(v)) return SLA_ERR_ALIGNMENT;
+  const size_t need = sla_linear_branch_ws_bytes(B, H, N, d, block);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  return from_hip(sla::launch_linear_prepare(k, v, B * H, (int)N, (int)d, block, (int)nb, marg_idx,
+                                             marg_cnt, km_max, ws, stream));
 }
 
 sla_status sla_linear_branch_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
@@ -157,8 +174,31 @@ sla_status sla_linear_branch_fwd(const uint16_t* q, const uint16_t* k, const uin
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_lin)) return SLA_ERR_ALIGNMENT;
   const size_t need = sla_linear_branch_ws_bytes(B, H, N, d, block);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
-  return from_hip(sla::launch_linear(q, k, v, B * H, (int)N, (int)d, block, (int)nb, marg_idx,
-                                     marg_cnt, km_max, o_lin, ws, stream));
+  st = from_hip(sla::launch_linear_prepare(k, v, B * H, (int)N, (int)d, block, (int)nb, marg_idx,
+                                           marg_cnt, km_max, ws, stream));
+  if (st != SLA_OK) return st;
+  return from_hip(sla::launch_linear_apply(q, B * H, (int)N, (int)d, block, (int)nb, ws, o_lin,
+                                           stream));
+}
+
+sla_status sla_sparse_linear_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                      int64_t B, int64_t H, int64_t N, int64_t d, int32_t block,
+                                      const int32_t* crit_idx, const int32_t* crit_cnt,
+                                      int32_t kc_max, float scale, const void* lin_ws,
+                                      size_t lin_ws_bytes, void* o, int32_t o_is_fp32, float* lse,
+                                      hipStream_t stream) {
+  int64_t nb = 0;
+  sla_status st = check_shape(B, H, N, d, block, &nb);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !v || !o || !crit_idx || !crit_cnt) return SLA_ERR_INVALID_ARG;
+  if (kc_max < 1 || kc_max > nb) return SLA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SLA_ERR_ALIGNMENT;
+  const size_t need = sla_linear_branch_ws_bytes(B, H, N, d, block);
+  if (!lin_ws || lin_ws_bytes < need || !aligned16(lin_ws)) return SLA_ERR_WORKSPACE;
+  return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
+                                   crit_cnt, kc_max, scale, o, o_is_fp32 != 0, lse, lin_ws,
+                                   stream));
 }
 
 sla_status sla_combine(const void* o_s, int32_t o_s_is_fp32, const float* o_lin, uint16_t* o,
@@ -181,6 +221,6 @@ const char* sla_status_string(sla_status status) {
   }
 }
 
-int32_t sla_version(void) { return 100; }
+int32_t sla_version(void) { return 200; }
 
 }  // extern "C"

@@ -16,20 +16,36 @@ hipError_t launch_select(const float* S, uint8_t* cls, int64_t rows, int nb, int
 hipError_t launch_block_mask(const uint8_t* cls, int64_t rows, int nkb, int32_t* crit_idx,
                              int32_t* crit_cnt, int kc_max, int32_t* marg_idx, int32_t* marg_cnt,
                              int km_max, int32_t* err_flag, hipStream_t s);
+// lin_ws: a linear-branch workspace after launch_linear_prepare, or NULL.
+// When given, each query's linear-branch output is added before the store.
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                        int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
-                       float scale, void* o, int o_fp32, float* lse, hipStream_t s);
+                       float scale, void* o, int o_fp32, float* lse, const void* lin_ws,
+                       hipStream_t s);
 // Linear-branch workspace: per-tile states H_j^T (bf16) and z_j (fp32), the
-// marginal bit matrix (words 32-bit words per query block) and the gathered
-// S_i^T (bf16), each piece 256-byte aligned.
+// marginal bit matrix (words 32-bit words per query block), zeta_i (fp32) and
+// the gathered S_i^T (bf16), each piece 256-byte aligned.
 struct LinearWs {
   int words;
-  size_t ht_bytes, z_bytes, bits_bytes, c_bytes, total;
+  size_t ht_bytes, z_bytes, bits_bytes, zeta_bytes, c_bytes, total;
+};
+struct LinearPtrs {
+  uint16_t* Ht;
+  float* Zs;
+  uint32_t* bits;
+  float* zeta;
+  uint16_t* C;
+  int words;
 };
 LinearWs linear_ws_layout(int64_t BH, int nb, int d);
-hipError_t launch_linear(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
-                         int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
-                         float* o_lin, void* ws, hipStream_t s);
+LinearPtrs linear_ws_ptrs(void* ws, int64_t BH, int nb, int d);
+// state, mask and gather: leaves S_i^T and zeta_i of every query block in ws
+hipError_t launch_linear_prepare(const uint16_t* k, const uint16_t* v, int64_t BH, int N, int d,
+                                 int block, int nb, const int32_t* idx, const int32_t* cnt,
+                                 int kmax, void* ws, hipStream_t s);
+// O_lin (fp32) from a prepared workspace
+hipError_t launch_linear_apply(const uint16_t* q, int64_t BH, int N, int d, int block, int nb,
+                               void* ws, float* o_lin, hipStream_t s);
 hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,
                           int64_t n_elems, hipStream_t s);
 

@@ -7,32 +7,21 @@
 //         LDS (the contraction runs over tokens) and multiplied on bf16 MFMA.
 //         H_j is stored transposed, bf16, as a row of the head's state matrix
 //         Ht[j][d2 * d + d1].
-// bits:   each query block's marginal list as a row of a bit matrix.
+// mask:   each query block's marginal list as a row of a bit matrix, and
+//         zeta_i = sum over the marked j of z_j (fp32, ascending j).
 // gather: S_i^T = sum over marginal j of H_j^T for every query block at once:
 //         C = M Ht with M the 0/1 marginal mask (exact in bf16), a GEMM on
 //         MFMA.  Ht is streamed through double-buffered LDS by asynchronous
 //         LDS-direct loads and read as the transposed operand; the mask bits
 //         become the bf16 1.0 / 0.0 operand in registers.
 // apply:  O_lin^T = S_i^T phi(Q_i)^T on MFMA, one query per lane, divided by
-//         phi(q) . zeta_i with zeta_i = sum over marginal j of z_j (fp32).
+//         phi(q) . zeta_i (linear_apply.h; the fused softmax kernels run the
+//         same step in their epilogue).
 #include "common.h"
 #include "launch.h"
+#include "linear_apply.h"
 
 namespace sla {
-
-__device__ __forceinline__ float phi(float x) { return x > 0.f ? x + 1.f : __expf(x); }
-
-// phi of 8 bf16 values, rounded back to bf16; tokens past the end give 0.
-__device__ __forceinline__ u32x4 phi8(u32x4 x, bool valid) {
-  u32x4 r;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float a = valid ? phi(bf16_bits_to_f32(x[e] & 0xffffu)) : 0.f;
-    const float b = valid ? phi(bf16_bits_to_f32(x[e] >> 16)) : 0.f;
-    r[e] = pack_bf16x2(a, b);
-  }
-  return r;
-}
 
 template <int D, int BLK>
 __global__ __launch_bounds__(256) void lin_state_kernel(const uint16_t* __restrict__ k,
@@ -121,14 +110,20 @@ __global__ __launch_bounds__(256) void lin_state_kernel(const uint16_t* __restri
   }
 }
 
-// Marginal list of each query block -> row of a bit matrix (W 32-bit words per
-// row, W even, W <= 128).  One wave per row; entries outside [0, nkb) are
-// dropped.
-__global__ __launch_bounds__(256) void lin_bits_kernel(const int32_t* __restrict__ idx,
+// Marginal list of each query block -> a row of the bit matrix (W 32-bit
+// words, W even, W <= 128) and zeta_i = sum of z_j over the set bits in
+// ascending j (fp32).  One wave per row; entries outside [0, nkb) are dropped
+// and a repeated entry counts once, as it does in the bit row.
+template <int D>
+__global__ __launch_bounds__(256) void lin_mask_kernel(const int32_t* __restrict__ idx,
                                                        const int32_t* __restrict__ cnt, int kmax,
-                                                       int64_t rows, int nkb, int W,
-                                                       uint32_t* __restrict__ bits) {
+                                                       int64_t rows, int nqb, int nkb, int W,
+                                                       const float* __restrict__ Zs,
+                                                       uint32_t* __restrict__ bits,
+                                                       float* __restrict__ zeta) {
+  constexpr int PER = D / 64;  // features per lane
   __shared__ uint32_t words[4][128];
+  __shared__ uint16_t js[4][4096];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t row = (int64_t)blockIdx.x * 4 + wv;
   if (row >= rows) return;
@@ -141,7 +136,55 @@ __global__ __launch_bounds__(256) void lin_bits_kernel(const int32_t* __restrict
     if (j >= 0 && j < nkb) atomicOr(&words[wv][j >> 5], 1u << (j & 31));
   }
   __builtin_amdgcn_wave_barrier();
-  for (int x = lane; x < W; x += 64) bits[row * W + x] = words[wv][x];
+
+  // bit row out; the set bits compacted to an ascending list of j in LDS
+  uint32_t w0 = lane < W ? words[wv][lane] : 0u;
+  uint32_t w1 = lane + 64 < W ? words[wv][lane + 64] : 0u;
+  if (lane < W) bits[row * W + lane] = w0;
+  if (lane + 64 < W) bits[row * W + lane + 64] = w1;
+  const int c0 = __popc(w0), c1 = __popc(w1);
+  int s0 = c0, s1 = c1;  // inclusive prefix sums over lanes
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t0 = __shfl_up(s0, o), t1 = __shfl_up(s1, o);
+    if (lane >= o) {
+      s0 += t0;
+      s1 += t1;
+    }
+  }
+  const int tot0 = __shfl(s0, 63);
+  const int total = tot0 + __shfl(s1, 63);
+  int p0 = s0 - c0, p1 = tot0 + s1 - c1;
+  while (w0) {
+    js[wv][p0++] = (uint16_t)(32 * lane + __ffs(w0) - 1);
+    w0 &= w0 - 1u;
+  }
+  while (w1) {
+    js[wv][p1++] = (uint16_t)(32 * (lane + 64) + __ffs(w1) - 1);
+    w1 &= w1 - 1u;
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  // zeta_i: 8 loads in flight, added strictly in list order
+  const float* zb = Zs + (row / nqb) * (int64_t)nkb * D + PER * lane;
+  float acc[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+  for (int t = 0; t < total; t += 8) {
+    float val[8][PER];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int j = js[wv][min(t + u, total - 1)];
+#pragma unroll
+      for (int e = 0; e < PER; ++e) val[u][e] = zb[j * D + e];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int e = 0; e < PER; ++e) acc[e] += t + u < total ? val[u][e] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) zeta[row * D + PER * lane + e] = acc[e];
 }
 
 // 8 mask bits -> 8 bf16 values 1.0 / 0.0 (the B operand of the gather GEMM).
@@ -248,65 +291,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// O_lin for one query block per workgroup, BLK / 32 waves of 32 queries.
 template <int D, int BLK>
-__global__ __launch_bounds__(256) void lin_apply_kernel(const uint16_t* __restrict__ q, int N,
-                                                        int nqb, int nkb,
-                                                        const int32_t* __restrict__ idx,
-                                                        const int32_t* __restrict__ cnt, int kmax,
-                                                        const uint16_t* __restrict__ C,
-                                                        const float* __restrict__ Zs,
-                                                        float* __restrict__ o_lin) {
-  __shared__ float zs[D];
-  __shared__ int used_s;
+__global__ __launch_bounds__(BLK * 2) void lin_apply_kernel(const uint16_t* __restrict__ q, int N,
+                                                            int nqb, const uint16_t* __restrict__ C,
+                                                            const float* __restrict__ zeta,
+                                                            float* __restrict__ o_lin) {
   const int64_t bh = blockIdx.x / nqb;
   const int qb = blockIdx.x % nqb;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int64_t head_off = bh * (int64_t)N * D;
-  const int count = min(cnt[bh * nqb + qb], kmax);
-  const int32_t* list = idx + (bh * nqb + qb) * (int64_t)kmax;
-
-  // zeta_i = sum of z_j over the marginal list (fp32)
-  if (tid < D) {
-    float zacc = 0.f;
-    int used = 0;
-    for (int t = 0; t < count; ++t) {
-      const int j = list[t];
-      if (j < 0 || j >= nkb) continue;
-      ++used;
-      zacc += Zs[(bh * nkb + j) * D + tid];
-    }
-    zs[tid] = zacc;
-    if (tid == 0) used_s = used;
-  }
-  __syncthreads();
-  if (32 * w >= BLK) return;
-
-  // O_lin^T = S_i^T phi(Q_i)^T; S_i^T rows (d2) come straight from C, d1-contiguous.
-  const uint16_t* St = C + (bh * nqb + qb) * (int64_t)D * D;
-  const int qrow = qb * BLK + 32 * w + l32;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, (uint32_t)N * D * 2);
-  f32x16 oacc[D / 32];
+  const int qrow = qb * BLK + 32 * w + l32;
+  u32x4 qf[D / 16];
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float den = 0.f;
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) {
-    const u32x4 pq = phi8(buf_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * hf) * 2), true);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d1 = 16 * ks + 8 * hf + 2 * e;
-      den = fmaf(bf16_bits_to_f32(pq[e] & 0xffffu), zs[d1], den);
-      den = fmaf(bf16_bits_to_f32(pq[e] >> 16), zs[d1 + 1], den);
-    }
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) {
-      const u32x4 a = *(const u32x4*)(St + (32 * db + l32) * D + 16 * ks + 8 * hf);
-      oacc[db] = mfma32x32x16(a, pq, oacc[db]);
-    }
-  }
-  den = sum_halves(den);
-  const float inv = (used_s > 0 && den > 0.f) ? 1.f / den : 0.f;
+  for (int ks = 0; ks < D / 16; ++ks)
+    qf[ks] = buf_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * hf) * 2);
+  f32x16 lacc[D / 32];
+  const int64_t row = bh * nqb + qb;
+  const float inv = linear_apply<D>(C + row * D * D, zeta + row * D, qf, l32, hf, lacc);
   if (qrow < N) {
     float* orow = o_lin + head_off + (int64_t)qrow * D;
 #pragma unroll
@@ -314,8 +318,8 @@ __global__ __launch_bounds__(256) void lin_apply_kernel(const uint16_t* __restri
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * db + 8 * g + 4 * hf;
-        *(f32x4*)(orow + d0) = f32x4{oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv,
-                                     oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv};
+        *(f32x4*)(orow + d0) = f32x4{lacc[db][4 * g] * inv, lacc[db][4 * g + 1] * inv,
+                                     lacc[db][4 * g + 2] * inv, lacc[db][4 * g + 3] * inv};
       }
   }
 }
@@ -356,53 +360,79 @@ LinearWs linear_ws_layout(int64_t BH, int nb, int d) {
   w.ht_bytes = up((size_t)BH * nb * d * d * 2);
   w.z_bytes = up((size_t)BH * nb * d * 4);
   w.bits_bytes = up((size_t)BH * nb * w.words * 4);
+  w.zeta_bytes = up((size_t)BH * nb * d * 4);
   w.c_bytes = up((size_t)BH * nb * d * d * 2);
-  w.total = w.ht_bytes + w.z_bytes + w.bits_bytes + w.c_bytes;
+  w.total = w.ht_bytes + w.z_bytes + w.bits_bytes + w.zeta_bytes + w.c_bytes;
   return w;
 }
 
-template <int D, int BLK>
-static hipError_t launch_linear_t(const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                                  int64_t BH, int N, int nb, const int32_t* idx, const int32_t* cnt,
-                                  int kmax, float* o_lin, void* ws, hipStream_t s) {
-  const LinearWs lw = linear_ws_layout(BH, nb, D);
+LinearPtrs linear_ws_ptrs(void* ws, int64_t BH, int nb, int d) {
+  const LinearWs lw = linear_ws_layout(BH, nb, d);
   char* p = static_cast<char*>(ws);
-  uint16_t* Ht = reinterpret_cast<uint16_t*>(p);
-  float* Zs = reinterpret_cast<float*>(p + lw.ht_bytes);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(p + lw.ht_bytes + lw.z_bytes);
-  uint16_t* C = reinterpret_cast<uint16_t*>(p + lw.ht_bytes + lw.z_bytes + lw.bits_bytes);
+  LinearPtrs r;
+  r.Ht = reinterpret_cast<uint16_t*>(p);
+  p += lw.ht_bytes;
+  r.Zs = reinterpret_cast<float*>(p);
+  p += lw.z_bytes;
+  r.bits = reinterpret_cast<uint32_t*>(p);
+  p += lw.bits_bytes;
+  r.zeta = reinterpret_cast<float*>(p);
+  p += lw.zeta_bytes;
+  r.C = reinterpret_cast<uint16_t*>(p);
+  r.words = lw.words;
+  return r;
+}
 
-  lin_state_kernel<D, BLK><<<dim3((unsigned)(BH * nb)), 256, 0, s>>>(k, v, N, nb, Ht, Zs);
+template <int D, int BLK>
+static hipError_t launch_linear_prepare_t(const uint16_t* k, const uint16_t* v, int64_t BH, int N,
+                                          int nb, const int32_t* idx, const int32_t* cnt, int kmax,
+                                          void* ws, hipStream_t s) {
+  const LinearPtrs lp = linear_ws_ptrs(ws, BH, nb, D);
+  lin_state_kernel<D, BLK><<<dim3((unsigned)(BH * nb)), 256, 0, s>>>(k, v, N, nb, lp.Ht, lp.Zs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = BH * nb;
-  lin_bits_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(idx, cnt, kmax, rows, nb,
-                                                                   lw.words, bits);
+  lin_mask_kernel<D><<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(idx, cnt, kmax, rows, nb, nb,
+                                                                      lp.words, lp.Zs, lp.bits,
+                                                                      lp.zeta);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int rowtiles = (nb + 127) / 128, coltiles = D * D / 128;
   const int64_t tiles = BH * rowtiles * coltiles;
   const int per_xcd = (int)((tiles + 7) / 8);
-  const size_t mbytes = (size_t)128 * (lw.words + 1) * sizeof(uint32_t);
+  const size_t mbytes = (size_t)128 * (lp.words + 1) * sizeof(uint32_t);
   lin_gather_kernel<D><<<dim3((unsigned)(per_xcd * 8)), 256, mbytes, s>>>(
-      Ht, bits, nb, nb, lw.words, rowtiles, coltiles, per_xcd, tiles, C);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  lin_apply_kernel<D, BLK><<<dim3((unsigned)(BH * nb)), 256, 0, s>>>(q, N, nb, nb, idx, cnt, kmax,
-                                                                    C, Zs, o_lin);
+      lp.Ht, lp.bits, nb, nb, lp.words, rowtiles, coltiles, per_xcd, tiles, lp.C);
   return hipGetLastError();
 }
 
-hipError_t launch_linear(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
-                         int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
-                         float* o_lin, void* ws, hipStream_t s) {
+hipError_t launch_linear_prepare(const uint16_t* k, const uint16_t* v, int64_t BH, int N, int d,
+                                 int block, int nb, const int32_t* idx, const int32_t* cnt,
+                                 int kmax, void* ws, hipStream_t s) {
   if (d == 128 && block == 128)
-    return launch_linear_t<128, 128>(q, k, v, BH, N, nb, idx, cnt, kmax, o_lin, ws, s);
+    return launch_linear_prepare_t<128, 128>(k, v, BH, N, nb, idx, cnt, kmax, ws, s);
   if (d == 128 && block == 64)
-    return launch_linear_t<128, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, o_lin, ws, s);
+    return launch_linear_prepare_t<128, 64>(k, v, BH, N, nb, idx, cnt, kmax, ws, s);
   if (d == 64 && block == 128)
-    return launch_linear_t<64, 128>(q, k, v, BH, N, nb, idx, cnt, kmax, o_lin, ws, s);
-  return launch_linear_t<64, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, o_lin, ws, s);
+    return launch_linear_prepare_t<64, 128>(k, v, BH, N, nb, idx, cnt, kmax, ws, s);
+  return launch_linear_prepare_t<64, 64>(k, v, BH, N, nb, idx, cnt, kmax, ws, s);
+}
+
+template <int D, int BLK>
+static hipError_t launch_linear_apply_t(const uint16_t* q, int64_t BH, int N, int nb, void* ws,
+                                        float* o_lin, hipStream_t s) {
+  const LinearPtrs lp = linear_ws_ptrs(ws, BH, nb, D);
+  lin_apply_kernel<D, BLK><<<dim3((unsigned)(BH * nb)), BLK * 2, 0, s>>>(q, N, nb, lp.C, lp.zeta,
+                                                                        o_lin);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_apply(const uint16_t* q, int64_t BH, int N, int d, int block, int nb,
+                               void* ws, float* o_lin, hipStream_t s) {
+  if (d == 128 && block == 128) return launch_linear_apply_t<128, 128>(q, BH, N, nb, ws, o_lin, s);
+  if (d == 128 && block == 64) return launch_linear_apply_t<128, 64>(q, BH, N, nb, ws, o_lin, s);
+  if (d == 64 && block == 128) return launch_linear_apply_t<64, 128>(q, BH, N, nb, ws, o_lin, s);
+  return launch_linear_apply_t<64, 64>(q, BH, N, nb, ws, o_lin, s);
 }
 
 hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,

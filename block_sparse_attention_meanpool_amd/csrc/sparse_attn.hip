@@ -13,8 +13,13 @@
 // Computing S^T (keys x queries) puts one query per lane, so row max, row sum
 // and the O rescale are per-lane values with a single exchange between the two
 // 32-lane halves of the wave.
+//
+// With a prepared linear-branch state, the epilogue also computes the
+// linear-attention output of the same queries from the Q registers it already
+// holds (linear_apply.h) and stores the sum of the two branches once.
 #include "common.h"
 #include "launch.h"
+#include "linear_apply.h"
 
 namespace sla {
 
@@ -22,7 +27,8 @@ template <int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
-    int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse, int seg) {
+    int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse, int seg,
+    const uint16_t* __restrict__ lin_C, const float* __restrict__ lin_zeta) {
   constexpr int NT = BLK * 2;   // threads
   constexpr int CH = D / 8;     // 16-byte chunks per K row
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * D];
@@ -168,6 +174,17 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const bool lin = lin_C != nullptr;
+  f32x16 lacc[D / 32];
+  float linv = 0.f;
+  if (lin) {
+    const int64_t row = bh * nqb + qb;
+    linv = linear_apply<D>(lin_C + row * D * D, lin_zeta + row * D, qf, l32, hf, lacc);
+  }
+  auto out = [&](int db, int r) {
+    const float x = oacc[db][r] * inv;
+    return lin ? x + lacc[db][r] * linv : x;
+  };
   if (qrow < N) {
     const int64_t obase = head_off + (int64_t)qrow * D;
 #pragma unroll
@@ -175,8 +192,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * db + 8 * g + 4 * hf;
-        const float x0 = oacc[db][4 * g] * inv, x1 = oacc[db][4 * g + 1] * inv;
-        const float x2 = oacc[db][4 * g + 2] * inv, x3 = oacc[db][4 * g + 3] * inv;
+        const float x0 = out(db, 4 * g), x1 = out(db, 4 * g + 1);
+        const float x2 = out(db, 4 * g + 2), x3 = out(db, 4 * g + 3);
         if (o_fp32) {
           *(f32x4*)((float*)o + obase + d0) = f32x4{x0, x1, x2, x3};
         } else {
@@ -299,7 +316,8 @@ __device__ __forceinline__ void compute_half(const char* kbuf, const char* vbuf,
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pipe_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
-    int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse, int seg) {
+    int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse, int seg,
+    const uint16_t* __restrict__ lin_C, const float* __restrict__ lin_zeta) {
   __shared__ __attribute__((aligned(1024))) char K0[BUFB];
   __shared__ __attribute__((aligned(1024))) char V0[BUFB];
   __shared__ __attribute__((aligned(1024))) char K1[BUFB];
@@ -360,6 +378,17 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   const float l_tot = sum_halves(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const bool lin = lin_C != nullptr;
+  f32x16 lacc[4];
+  float linv = 0.f;
+  if (lin) {
+    const int64_t row = bh * nqb + qb;
+    linv = linear_apply<D>(lin_C + row * D * D, lin_zeta + row * D, qf, l32, hf, lacc);
+  }
+  auto out = [&](int db, int r) {
+    const float x = oacc[db][r] * inv;
+    return lin ? x + lacc[db][r] * linv : x;
+  };
   if (qrow < N) {
     const int64_t obase = head_off + (int64_t)qrow * D;
 #pragma unroll
@@ -367,8 +396,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int d0 = 32 * db + 8 * g + 4 * hf;
-        const float x0 = oacc[db][4 * g] * inv, x1 = oacc[db][4 * g + 1] * inv;
-        const float x2 = oacc[db][4 * g + 2] * inv, x3 = oacc[db][4 * g + 3] * inv;
+        const float x0 = out(db, 4 * g), x1 = out(db, 4 * g + 1);
+        const float x2 = out(db, 4 * g + 2), x3 = out(db, 4 * g + 3);
         if (o_fp32) {
           *(f32x4*)((float*)o + obase + d0) = f32x4{x0, x1, x2, x3};
         } else {
@@ -385,28 +414,41 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 template <int D, int BLK>
 static hipError_t launch_attn_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
                                 int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
-                                float scale, void* o, int o_fp32, float* lse, hipStream_t s) {
+                                float scale, void* o, int o_fp32, float* lse,
+                                const uint16_t* lin_C, const float* lin_zeta, hipStream_t s) {
   const int seg = (nb + 7) / 8;
   dim3 grid((unsigned)(BH * seg * 8));
   attn_fwd_kernel<D, BLK><<<grid, BLK * 2, 0, s>>>(q, k, v, N, nb, nb, idx, cnt, kmax,
-                                                    scale * kLog2e, o, o_fp32, lse, seg);
+                                                    scale * kLog2e, o, o_fp32, lse, seg, lin_C,
+                                                    lin_zeta);
   return hipGetLastError();
 }
 
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                        int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
-                       float scale, void* o, int o_fp32, float* lse, hipStream_t s) {
+                       float scale, void* o, int o_fp32, float* lse, const void* lin_ws,
+                       hipStream_t s) {
+  const uint16_t* lin_C = nullptr;
+  const float* lin_zeta = nullptr;
+  if (lin_ws) {
+    const LinearPtrs lp = linear_ws_ptrs(const_cast<void*>(lin_ws), BH, nb, d);
+    lin_C = lp.C;
+    lin_zeta = lp.zeta;
+  }
   if (d == 128 && block == 128) {
     const int seg = (nb + 7) / 8;
     pipe::attn_fwd_pipe_kernel<<<dim3((unsigned)(BH * seg * 8)), pipe::NT, 0, s>>>(
-        q, k, v, N, nb, nb, idx, cnt, kmax, scale * kLog2e, o, o_fp32, lse, seg);
+        q, k, v, N, nb, nb, idx, cnt, kmax, scale * kLog2e, o, o_fp32, lse, seg, lin_C, lin_zeta);
     return hipGetLastError();
   }
   if (d == 128 && block == 64)
-    return launch_attn_t<128, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, s);
+    return launch_attn_t<128, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, lin_C,
+                                  lin_zeta, s);
   if (d == 64 && block == 128)
-    return launch_attn_t<64, 128>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, s);
-  return launch_attn_t<64, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, s);
+    return launch_attn_t<64, 128>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, lin_C,
+                                  lin_zeta, s);
+  return launch_attn_t<64, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, lin_C,
+                               lin_zeta, s);
 }
 
 }  // namespace sla

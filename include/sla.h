@@ -146,7 +146,8 @@ sla_status sla_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
  *   per query block i: S_i = sum_{j in marg_i} H_j, zeta_i = sum z_j;
  *   O_lin[n] = phi(q_n)^T S_i / (phi(q_n) . zeta_i).
  * A row with marg_cnt = 0 gets O_lin = 0.  phi(q), phi(k) and S_i enter bf16
- * MFMA products; sums are fp32.
+ * MFMA products; sums are fp32.  Entries outside [0, nb) are ignored and a
+ * repeated entry counts once.
  *
  * o_lin     fp32 [B, H, N, d]                                   (out)
  * ws        device workspace of at least sla_linear_branch_ws_bytes() bytes
@@ -156,8 +157,46 @@ sla_status sla_linear_branch_fwd(const uint16_t* q, const uint16_t* k, const uin
                                  const int32_t* marg_idx, const int32_t* marg_cnt, int32_t km_max,
                                  float* o_lin, void* ws, size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes for sla_linear_branch_fwd (the per-tile states H_j, z_j). */
+/* Workspace bytes for sla_linear_branch_fwd and sla_linear_branch_prepare:
+ * the per-tile states H_j (bf16) and z_j (fp32), the marginal bit matrix, and
+ * the per-query-block S_i (bf16) and zeta_i (fp32).  0 for unsupported
+ * arguments. */
 size_t sla_linear_branch_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block);
+
+/*
+ * The query-independent half of the linear branch (SLA post: intermediate
+ * blocks via linear attention): the per-tile states H_j, z_j and, for every
+ * query block i, S_i = sum_{j in marg_i} H_j and zeta_i = sum z_j, left in
+ * `ws` for sla_sparse_linear_attn_fwd.  Same arguments and rules as
+ * sla_linear_branch_fwd; entries outside [0, nb) are ignored and a repeated
+ * entry counts once.  The workspace contents are opaque and stay valid until
+ * the caller reuses the buffer.
+ */
+sla_status sla_linear_branch_prepare(const uint16_t* k, const uint16_t* v, int64_t B, int64_t H,
+                                     int64_t N, int64_t d, int32_t block, const int32_t* marg_idx,
+                                     const int32_t* marg_cnt, int32_t km_max, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Both branches of one SLA layer in one pass (SLA post: critical blocks via
+ * FlashAttention, intermediate blocks via linear attention, the results
+ * added): O = O_s + O_lin, with O_s as in sla_sparse_attn_fwd and O_lin as in
+ * sla_linear_branch_fwd, taken from a workspace that sla_linear_branch_prepare
+ * filled for the same K, V, shapes and marginal lists.  Each query's two
+ * outputs are summed in fp32 and stored once; this replaces the separate
+ * linear apply, the fp32 O_s / O_lin buffers and sla_combine.
+ *
+ * lin_ws    prepared linear-branch workspace (in), at least
+ *           sla_linear_branch_ws_bytes() bytes
+ * o         [B, H, N, d]; fp32 when o_is_fp32 != 0, else bf16 (RNE) (out)
+ * lse       fp32 [B, H, N] of the softmax branch, or NULL         (out)
+ */
+sla_status sla_sparse_linear_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                      int64_t B, int64_t H, int64_t N, int64_t d, int32_t block,
+                                      const int32_t* crit_idx, const int32_t* crit_cnt,
+                                      int32_t kc_max, float scale, const void* lin_ws,
+                                      size_t lin_ws_bytes, void* o, int32_t o_is_fp32, float* lse,
+                                      hipStream_t stream);
 
 /*
  * Sum the branches and round to bf16: O = bf16_rne(O_s + O_lin).  The pages

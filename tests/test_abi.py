@@ -96,9 +96,9 @@ def test_workspace_sizes(mod):
     assert lib.sla_pool_classify_ws_bytes(1, 2, 1024, 64, 64, 0) == 2048 + 16384
     assert lib.sla_pool_classify_ws_bytes(1, 2, 1024, 96, 64, 0) == 0
     # bf16 states H_j^T [8, 128*128], fp32 z_j [8, 128], bit rows [8, 2 words] (256-byte
-    # aligned), bf16 gathered S_i^T [8, 128*128]
+    # aligned), fp32 zeta_i [8, 128], bf16 gathered S_i^T [8, 128*128]
     assert lib.sla_linear_branch_ws_bytes(1, 1, 1000, 128, 128) == \
-        8 * 128 * 128 * 2 + 8 * 128 * 4 + 256 + 8 * 128 * 128 * 2
+        8 * 128 * 128 * 2 + 8 * 128 * 4 + 256 + 8 * 128 * 4 + 8 * 128 * 128 * 2
 
 
 def test_other_entry_points_reject_bad_arguments(mod):
@@ -122,6 +122,24 @@ def test_other_entry_points_reject_bad_arguments(mod):
     assert lb(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, GOOD, None, 0, None) == -4
     assert lb(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 0, GOOD, GOOD, 1 << 40, None) == -1
     assert lb(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, ODD, GOOD, 1 << 40, None) == -3
+    # linear prepare
+    lp = lib.sla_linear_branch_prepare
+    assert lp(GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, None, 0, None) == -4
+    assert lp(GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, GOOD, 16, None) == -4
+    assert lp(None, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, GOOD, 1 << 40, None) == -1
+    assert lp(GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 5, GOOD, 1 << 40, None) == -1
+    assert lp(GOOD, ODD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, GOOD, 1 << 40, None) == -3
+    assert lp(GOOD, GOOD, 1, 1, 256, 96, 64, GOOD, GOOD, 2, GOOD, 1 << 40, None) == -2
+    # fused sparse + linear
+    fz = lib.sla_sparse_linear_attn_fwd
+    args = [GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, 0.125, GOOD, 1 << 40, GOOD, 0,
+            None, None]
+    # every call below fails validation before anything is launched
+    for pos, val, want in ((12, None, -4), (13, 16, -4), (14, None, -1), (8, None, -1),
+                           (10, 5, -1), (11, 0.0, -1), (14, ODD, -3), (6, 80, -2)):
+        bad = list(args)
+        bad[pos] = val
+        assert fz(*bad) == want, (pos, val)
     # combine
     assert lib.sla_combine(GOOD, 1, None, GOOD, 12, None) == -1
     assert lib.sla_combine(GOOD, 1, ODD, GOOD, 16, None) == -3

@@ -94,6 +94,11 @@ def test_workload_parity(name):
     o_s, lse = sla.sla_sparse_attn_fwd(q, k, v, b, ci, cc, o_fp32=True, want_lse=True)
     o_lin = sla.sla_linear_branch_fwd(q, k, v, b, mi, mc) if km else None
     o = sla.sla_combine(o_s, o_lin)
+    fused = None
+    if km:
+        lin_ws = sla.sla_linear_branch_prepare(k, v, b, mi, mc)
+        fused, _ = sla.sla_sparse_linear_attn_fwd(q, k, v, b, ci, cc, lin_ws, o_fp32=True)
+        del lin_ws
     torch.cuda.synchronize()
     assert flag.item() == 0
     idx_ref, cnt_ref = osla.index_lists(cls_ref, osla.CRITICAL, kc_max)
@@ -112,6 +117,7 @@ def test_workload_parity(name):
         rows = _sample_rows(spec, SAMPLES_PER_HEAD[name])
     t0 = time.time()
     got_s, got_lse, got_lin, got_o, want_s, want_lse, want_lin, want_o = ([] for _ in range(8))
+    got_f = []
     heads = {}
     for (bb, h, i) in rows:
         if (bb, h) not in heads:
@@ -126,6 +132,8 @@ def test_workload_parity(name):
         got_lse.append(lse[bb, h, lo:hi].cpu().numpy())
         got_lin.append(np.zeros_like(r_lin) if o_lin is None else o_lin[bb, h, lo:hi].cpu().numpy())
         got_o.append(o[bb, h, lo:hi].cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
+        if fused is not None:
+            got_f.append(fused[bb, h, lo:hi].cpu().numpy())
     say(f"  oracle outputs for {len(rows)} query blocks in {time.time() - t0:.1f} s")
     cat = np.concatenate
     check_close(cat(got_s), cat(want_s), "O_s")
@@ -136,3 +144,5 @@ def test_workload_parity(name):
     check_close(pre, cat(want_o), "O (fp32, pre-rounding)")
     np.testing.assert_array_equal(cat(got_o), rne_bf16_bits(pre))
     check_close(osla.bf16_to_f64(cat(got_o)), cat(want_o), "O (bf16)", max_abs=4e-2, rel_l2=8e-3)
+    if fused is not None:
+        check_close(cat(got_f), cat(want_o), "O fused (fp32)")

@@ -4,6 +4,8 @@ Every stage of the path is compared with the fp64 oracle through the C ABI:
 pooled Q/K (fp32 diagnostic), class map and lists (bit-exact), the sparse
 branch and its LSE, the linear branch, and the combined output (bars on the
 fp32 pre-rounding output; the bf16 output must be its exact RNE rounding).
+Where a linear branch exists, the fused call (prepare + sparse_linear_attn)
+is held to the same bars and to the unfused sum.
 """
 
 from fractions import Fraction as F
@@ -57,9 +59,16 @@ def case(request):
     o_s16, _ = sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt, o_fp32=False)
     o_lin = sla.sla_linear_branch_fwd(q, k, v, b, marg_idx, marg_cnt) if km else None
     o = sla.sla_combine(o_s, o_lin)
+    fused32 = fused16 = None
+    if km:
+        lin_ws = sla.sla_linear_branch_prepare(k, v, b, marg_idx, marg_cnt)
+        fused32, _ = sla.sla_sparse_linear_attn_fwd(q, k, v, b, crit_idx, crit_cnt, lin_ws,
+                                                    o_fp32=True)
+        fused16, _ = sla.sla_sparse_linear_attn_fwd(q, k, v, b, crit_idx, crit_cnt, lin_ws)
+        fused32, fused16 = fused32.cpu().numpy(), bits_of(fused16)
     torch.cuda.synchronize()
     return dict(spec=spec, kc=kc, km=km, kc_max=kc_max, cls_ref=cls_ref, qp_ref=qp_ref,
-                kp_ref=kp_ref, ref=ref, qp=f64(qp), kp=f64(kp), cls=cls.cpu().numpy(),
+                kp_ref=kp_ref, fused32=fused32, fused16=fused16, ref=ref, qp=f64(qp), kp=f64(kp), cls=cls.cpu().numpy(),
                 crit_idx=crit_idx.cpu().numpy(), crit_cnt=crit_cnt.cpu().numpy(),
                 marg_idx=None if marg_idx is None else marg_idx.cpu().numpy(),
                 marg_cnt=None if marg_cnt is None else marg_cnt.cpu().numpy(),
@@ -109,3 +118,17 @@ def test_combined_output(case):
     check_close(pre, o_ref, "O (fp32, pre-rounding)")
     np.testing.assert_array_equal(case["o"], rne_bf16_bits(pre))
     check_close(osla.bf16_to_f64(case["o"]), o_ref, "O (bf16)", max_abs=4e-2, rel_l2=8e-3)
+
+
+def test_fused_output(case):
+    if not case["km"]:
+        pytest.skip("no marginal blocks in this workload")
+    _, _, _, o_ref = case["ref"]
+    f32 = case["fused32"]
+    check_close(f32, o_ref, "O fused (fp32)")
+    np.testing.assert_array_equal(case["fused16"], rne_bf16_bits(f32))
+    # the same two fp32 branch outputs, summed without the intermediate rounding
+    # of each: a few fp32 ulps of their magnitudes apart
+    o_s, o_lin = case["o_s"].astype(np.float64), case["o_lin"].astype(np.float64)
+    bound = 4 * 2.0 ** -24 * (np.abs(o_s) + np.abs(o_lin)) + 1e-30
+    assert np.all(np.abs(f32 - (o_s + o_lin)) <= bound)

@@ -133,6 +133,31 @@ def test_list_order_does_not_matter(data):
     check_close(b.cpu().numpy(), o_ref, "O_s, descending list")
 
 
+def test_marginal_list_repeats_and_strays(data):
+    """A repeated marginal entry counts once and entries outside [0, nb) are
+    ignored, in the standalone and the fused linear branch alike."""
+    q, k, v = (to_dev(data[t]) for t in "qkv")
+    nb = SPEC.nb
+    cls = sla.sla_pool_classify(q, k, 128, "sla3", 2, 3)
+    ci, cc, mi, mc = sla.sla_block_mask(cls, 2, 3)
+    wide = torch.full(mi.shape[:-1] + (7,), -1, dtype=torch.int32, device="cuda")
+    wide[..., :3] = mi
+    wide[..., 3] = mi[..., 1]          # a repeat
+    wide[..., 4] = nb + 5              # past the last block
+    wide[..., 5] = -3
+    wide[..., 6] = mi[..., 0]          # another repeat
+    wc = torch.full_like(mc, 7)
+    a = sla.sla_linear_branch_fwd(q, k, v, 128, mi, mc)
+    b = sla.sla_linear_branch_fwd(q, k, v, 128, wide, wc)
+    ws_a = sla.sla_linear_branch_prepare(k, v, 128, mi, mc)
+    fa, _ = sla.sla_sparse_linear_attn_fwd(q, k, v, 128, ci, cc, ws_a, o_fp32=True)
+    ws_b = sla.sla_linear_branch_prepare(k, v, 128, wide, wc)
+    fb, _ = sla.sla_sparse_linear_attn_fwd(q, k, v, 128, ci, cc, ws_b, o_fp32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    assert torch.equal(fa, fb)
+
+
 def test_forward_pipeline_matches_stages(data):
     q, k, v = (to_dev(data[t]) for t in "qkv")
     out = sla.forward(q, k, v, 128, "sla3", keep=F(2, 8), marg=F(3, 8))
@@ -144,6 +169,11 @@ def test_forward_pipeline_matches_stages(data):
     torch.cuda.synchronize()
     assert torch.equal(out["cls"], cls)
     assert torch.equal(bits_of_t(out["o"]), bits_of_t(o))
+    fused = sla.forward(q, k, v, 128, "sla3", keep=F(2, 8), marg=F(3, 8), fused=True)
+    ws = sla.sla_linear_branch_prepare(k, v, 128, mi, mc)
+    of, _ = sla.sla_sparse_linear_attn_fwd(q, k, v, 128, ci, cc, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(bits_of_t(fused["o"]), bits_of_t(of))
     out2 = sla.forward(q, k, v, 128, "topk", keep=F(1, 4))
     o2, _ = sla.sla_sparse_attn_fwd(q, k, v, 128, out2["crit_idx"], out2["crit_cnt"], o_fp32=True)
     torch.cuda.synchronize()
