@@ -132,7 +132,7 @@ def cpu_baseline(spec, data, kc, km, budget_s=20.0):
         k = osla.bf16_to_f64(data["k"][0, h])[None, None]
         v = osla.bf16_to_f64(data["v"][0, h])[None, None]
         cls, *_ = osla.class_map(q, k, spec.block, sel, spec.keep, spec.marg, spec.thr)
-        rows = [(0, 0, int(i)) for i in g.choice(spec.nb, size=min(spec.nb, 64), replace=False)]
+        rows = [(0, 0, int(i)) for i in g.choice(spec.nb, size=min(spec.nb, 128), replace=False)]
         osla.forward_rows(q, k, v, cls, spec.block, rows)
         for (_, _, i) in rows:
             lo, hi = osla.block_bounds(spec.N, spec.block, i)
@@ -145,7 +145,7 @@ def cpu_baseline(spec, data, kc, km, budget_s=20.0):
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": (f"fp64 numpy oracle: pool + score + top-k class map of {h} head(s) in full, "
                        f"then masked softmax attention of {blocks} sampled query blocks "
-                       f"(64 per head); kept-block FLOP of those blocks / wall time "
+                       f"(128 per head); kept-block FLOP of those blocks / wall time "
                        f"({dt:.1f} s)")}
 
 

@@ -23,7 +23,9 @@
 
 namespace sla {
 
-template <int D, int BLK>
+// LIST: key tiles from the per-query-block lists (sparse); otherwise every
+// tile in order (the dense baseline, a separate instantiation).
+template <int D, int BLK, bool LIST>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
@@ -58,8 +60,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int ks = 0; ks < D / 16; ++ks)
     qf[ks] = buf_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * hf) * 2);
 
-  const int count = idx ? min(cnt[bh * nqb + qb], kmax) : nkb;
-  const int32_t* list = idx ? idx + (bh * nqb + qb) * (int64_t)kmax : nullptr;
+  const int count = LIST ? min(cnt[bh * nqb + qb], kmax) : nkb;
+  const int32_t* list = LIST ? idx + (bh * nqb + qb) * (int64_t)kmax : nullptr;
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int krow = swap_bits_2_3(l32);
 
   for (int t = 0; t < count; ++t) {
-    const int j = list ? list[t] : t;
+    const int j = LIST ? list[t] : t;
     if (j < 0 || j >= nkb) continue;  // ignore entries outside the key-block range
     __syncthreads();  // previous tile's LDS reads are done
     // K tile, row-major, swizzled chunks.
@@ -313,6 +315,7 @@ __device__ __forceinline__ void compute_half(const char* kbuf, const char* vbuf,
   (void)l32;
 }
 
+template <bool LIST>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_pipe_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
@@ -341,10 +344,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   c.w = w;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
 
-  const int count = idx ? min(cnt[bh * nqb + qb], kmax) : nkb;
-  const int32_t* list = idx ? idx + (bh * nqb + qb) * (int64_t)kmax : nullptr;
+  const int count = LIST ? min(cnt[bh * nqb + qb], kmax) : nkb;
+  const int32_t* list = LIST ? idx + (bh * nqb + qb) * (int64_t)kmax : nullptr;
 
-  int j_cur = count > 0 ? (list ? list[0] : 0) : 0;
+  int j_cur = count > 0 ? (LIST ? list[0] : 0) : 0;
   if (count > 0) issue_half(c, j_cur, 0, K0, V0);
 
   const int qrow = qb * BLK + 32 * w + l32;
@@ -361,7 +364,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const bool ok = j_cur >= 0 && j_cur < nkb;
     // next tile index: loaded before the wait below, which drains it together
     // with the loads of buffer 0
-    const int j_next = (t + 1 < count) ? (list ? list[t + 1] : t + 1) : 0;
+    const int j_next = (t + 1 < count) ? (LIST ? list[t + 1] : t + 1) : 0;
     // first half of tile j_cur, in buffer 0
     wait_vm0();
     __syncthreads();  // buffer 0 complete; every wave is done with buffer 1
@@ -418,9 +421,14 @@ static hipError_t launch_attn_t(const uint16_t* q, const uint16_t* k, const uint
                                 const uint16_t* lin_C, const float* lin_zeta, hipStream_t s) {
   const int seg = (nb + 7) / 8;
   dim3 grid((unsigned)(BH * seg * 8));
-  attn_fwd_kernel<D, BLK><<<grid, BLK * 2, 0, s>>>(q, k, v, N, nb, nb, idx, cnt, kmax,
-                                                    scale * kLog2e, o, o_fp32, lse, seg, lin_C,
-                                                    lin_zeta);
+  if (idx)
+    attn_fwd_kernel<D, BLK, true><<<grid, BLK * 2, 0, s>>>(q, k, v, N, nb, nb, idx, cnt, kmax,
+                                                          scale * kLog2e, o, o_fp32, lse, seg,
+                                                          lin_C, lin_zeta);
+  else
+    attn_fwd_kernel<D, BLK, false><<<grid, BLK * 2, 0, s>>>(q, k, v, N, nb, nb, idx, cnt, kmax,
+                                                           scale * kLog2e, o, o_fp32, lse, seg,
+                                                           lin_C, lin_zeta);
   return hipGetLastError();
 }
 
@@ -437,8 +445,13 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
   }
   if (d == 128 && block == 128) {
     const int seg = (nb + 7) / 8;
-    pipe::attn_fwd_pipe_kernel<<<dim3((unsigned)(BH * seg * 8)), pipe::NT, 0, s>>>(
-        q, k, v, N, nb, nb, idx, cnt, kmax, scale * kLog2e, o, o_fp32, lse, seg, lin_C, lin_zeta);
+    const dim3 grid((unsigned)(BH * seg * 8));
+    if (idx)
+      pipe::attn_fwd_pipe_kernel<true><<<grid, pipe::NT, 0, s>>>(
+          q, k, v, N, nb, nb, idx, cnt, kmax, scale * kLog2e, o, o_fp32, lse, seg, lin_C, lin_zeta);
+    else
+      pipe::attn_fwd_pipe_kernel<false><<<grid, pipe::NT, 0, s>>>(
+          q, k, v, N, nb, nb, idx, cnt, kmax, scale * kLog2e, o, o_fp32, lse, seg, lin_C, lin_zeta);
     return hipGetLastError();
   }
   if (d == 128 && block == 64)
