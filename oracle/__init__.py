@@ -17,15 +17,19 @@ What it computes, and where the pages say so:
 * Veda article (page 5, "what happened"): attention is computed only on the
   128-token key tiles selected for each query.
 
+* SLA post ("results"): the method is trainable with a short fine-tuning;
+  ``grad.py`` holds the gradients of the forward with the class map fixed.
+
 Every function is the plain definition, in fp64, with numpy BLAS matmuls as
 the only library step.  Readings of points the pages leave open are listed in
 ``sla.py``'s header.
 
 Parity status: every function here is pinned by the CPU tests (closed forms,
 brute-force enumeration, special cases that reduce to library routines,
-invariants, hand-derived fixtures under tests/golden).  The end-to-end values
+invariants, hand-derived fixtures under tests/golden; the gradients by central
+finite differences and by torch autograd of dense attention).  The end-to-end values
 on the structured workloads have no published number to hit; they are pinned
 only through those parts.
 """
 
-from . import sla  # noqa: F401
+from . import grad, sla  # noqa: F401

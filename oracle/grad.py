@@ -1,0 +1,124 @@
+"""Gradients of the oracle forward with the class map held fixed (fp64).
+
+TEST INFRASTRUCTURE ONLY (see the package header).
+
+The SLA post ("results") says the method is trainable and needs only a short
+fine-tuning; these are the gradients that training would use.  The block
+selection is a discrete choice made before the attention, so it is held fixed:
+the gradient flows through the two branches that the class map routes each
+query block to, and the sum O = O_s + O_lin passes dO to both unchanged (R10).
+
+Softmax branch, per query block with its critical tokens T (R11):
+    P = softmax(scale Q K_T^T),  O_s = P V_T
+    dV_T = P^T dO,   dP = dO V_T^T,   dS = P * (dP - rowsum(dO * O_s))
+    dQ = scale dS K_T,   dK_T = scale dS^T Q
+
+Linear branch, per query block with its marginal tokens M (R9):
+    a = phi(Q), Phi = phi(K_M), S = Phi^T V_M, zeta = Phi^T 1
+    u = a S, w = a zeta, O_lin = u / w
+    dU = dO / w,   dw = -rowsum(dO * O_lin) / w
+    da = dU S^T + dw zeta^T,      dQ = da * phi'(Q)
+    dS = a^T dU,   dzeta = a^T dw
+    dPhi = V_M dS^T + 1 dzeta^T,  dV_M = Phi dS,   dK_M = dPhi * phi'(K_M)
+with phi'(x) = 1 for x > 0 and exp(x) otherwise.
+
+Keys and values receive the sum over every query block whose lists contain
+their tile.  A query block with an empty branch gets nothing from it (R12).
+"""
+
+import math
+
+import numpy as np
+
+from . import sla
+
+
+def dphi(x):
+    """Derivative of elu(x) + 1 (alpha = 1): 1 for x > 0, exp(x) otherwise."""
+    x = np.asarray(x, dtype=np.float64)
+    return np.where(x > 0, 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def attend_block_grad(q_rows, k, v, kept_blocks, b, scale, d_o):
+    """Gradient of the masked softmax attention of one query block.
+
+    Returns (dq [r, d], toks, dk_toks [|T|, d], dv_toks [|T|, d]).
+    """
+    N = k.shape[0]
+    toks = sla._tokens_of(kept_blocks, N, b)
+    r, d = q_rows.shape
+    if len(toks) == 0:
+        z = np.zeros((0, d))
+        return np.zeros((r, d)), toks, z, np.zeros((0, v.shape[1]))
+    o, _, p = sla.attend_block(q_rows, k, v, kept_blocks, b, scale, return_p=True)
+    kt, vt = k[toks], v[toks]
+    dv = p.T @ d_o
+    dp = d_o @ vt.T
+    delta = (d_o * o).sum(axis=1, keepdims=True)
+    ds = p * (dp - delta)
+    dq = scale * (ds @ kt)
+    dk = scale * (ds.T @ q_rows)
+    return dq, toks, dk, dv
+
+
+def linear_block_grad(q_rows, k, v, marg_blocks, b, d_o):
+    """Gradient of the linear attention of one query block.
+
+    Returns (dq [r, d], toks, dk_toks [|M|, d], dv_toks [|M|, d]).
+    """
+    N = k.shape[0]
+    toks = sla._tokens_of(marg_blocks, N, b)
+    r, d = q_rows.shape
+    if len(toks) == 0:
+        return np.zeros((r, d)), toks, np.zeros((0, d)), np.zeros((0, v.shape[1]))
+    km, vm = k[toks], v[toks]
+    a = sla.phi(q_rows)
+    ph = sla.phi(km)
+    state = ph.T @ vm
+    zeta = ph.sum(axis=0)
+    u = a @ state
+    w = a @ zeta
+    o_lin = u / w[:, None]
+    du = d_o / w[:, None]
+    dw = -(d_o * o_lin).sum(axis=1) / w
+    da = du @ state.T + np.outer(dw, zeta)
+    dq = da * dphi(q_rows)
+    dstate = a.T @ du
+    dzeta = a.T @ dw
+    dph = vm @ dstate.T + dzeta[None, :]
+    dv = ph @ dstate
+    dk = dph * dphi(km)
+    return dq, toks, dk, dv
+
+
+def backward(q, k, v, cls, b, d_o, scale=None, branches=("softmax", "linear")):
+    """dQ, dK, dV (float64 [B, H, N, d]) of sum(O * d_o) with O from sla.forward.
+
+    `branches` restricts the gradient to one branch (the same sum with the
+    other branch's output held constant).
+    """
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nqb = sla.num_blocks(N, b)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for bi in range(B):
+        for h in range(H):
+            for i in range(nqb):
+                lo, hi = sla.block_bounds(N, b, i)
+                qr, g = q[bi, h, lo:hi], d_o[bi, h, lo:hi]
+                if "softmax" in branches:
+                    crit = np.nonzero(cls[bi, h, i] == sla.CRITICAL)[0]
+                    a, toks, ck, cv = attend_block_grad(qr, k[bi, h], v[bi, h], crit, b, scale, g)
+                    dq[bi, h, lo:hi] += a
+                    np.add.at(dk[bi, h], toks, ck)
+                    np.add.at(dv[bi, h], toks, cv)
+                if "linear" in branches:
+                    marg = np.nonzero(cls[bi, h, i] == sla.MARGINAL)[0]
+                    a, toks, ck, cv = linear_block_grad(qr, k[bi, h], v[bi, h], marg, b, g)
+                    dq[bi, h, lo:hi] += a
+                    np.add.at(dk[bi, h], toks, ck)
+                    np.add.at(dv[bi, h], toks, cv)
+    return dq, dk, dv
