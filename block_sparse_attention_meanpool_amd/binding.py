@@ -45,6 +45,9 @@ _SIGS = {
     "sla_sparse_linear_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32,
                                           _F, _P, _SZ, _P, _I32, _P, _P]),
     "sla_combine": (_I32, [_P, _I32, _P, _P, _I64, _P]),
+    "sla_sparse_attn_bwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _F, _P,
+                                   _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "sla_sparse_attn_bwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32]),
     "sla_dense_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _F, _P, _I32, _P, _P]),
     "sla_status_string": (ctypes.c_char_p, [_I32]),
     "sla_version": (_I32, []),
@@ -252,6 +255,28 @@ def sla_sparse_linear_attn_fwd(q, k, v, block, crit_idx, crit_cnt, lin_ws, scale
           _ptr(crit_idx), _ptr(crit_cnt), crit_idx.shape[-1], float(scale), _ptr(lin_ws),
           lin_ws.numel(), _ptr(o), int(o.dtype == torch.float32), _ptr(lse), _stream(stream))
     return o, lse
+
+
+def sla_sparse_attn_bwd(q, k, v, block, crit_idx, crit_cnt, o_s, lse, d_o, scale=None, dq=None,
+                        dk=None, dv=None, ws=None, stream=None):
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
+        _dev(t, torch.bfloat16, n)
+    _dev(crit_idx, torch.int32, "crit_idx")
+    _dev(crit_cnt, torch.int32, "crit_cnt")
+    _dev(lse, torch.float32, "lse")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) if t is None else t
+                  for t in (dq, dk, dv))
+    need = lib().sla_sparse_attn_bwd_ws_bytes(B, H, N, d, block)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _call("sla_sparse_attn_bwd", _ptr(q), _ptr(k), _ptr(v), B, H, N, d, block, _ptr(crit_idx),
+          _ptr(crit_cnt), crit_idx.shape[-1], float(scale), _ptr(o_s),
+          int(o_s.dtype == torch.float32), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
+          _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    return dq, dk, dv
 
 
 def sla_combine(o_s, o_lin=None, o=None, stream=None):

@@ -156,9 +156,24 @@ typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
 __device__ __forceinline__ int trs_swz(int r) { return (0xAC60 >> (4 * (r & 3))) & 15; }
 
+// A swizzle that serves both access kinds of a 256-byte-row tile: the
+// transpose reads above (rows 4a..4a+3 must differ in bits 2-3 of the
+// swizzle) and MFMA operand row reads (16 consecutive rows, one chunk: the
+// swizzle must be a bijection on r % 16).  Swapping the two 2-bit halves of
+// r % 16 does both.  Used by tiles that are read both ways.
+__device__ __forceinline__ int dual_swz(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+
+struct TrSwz {
+  __device__ static int f(int r) { return trs_swz(r); }
+};
+struct DualSwz {
+  __device__ static int f(int r) { return dual_swz(r); }
+};
+
+template <class SW = TrSwz>
 __device__ __forceinline__ u32x2 tr_read256(const char* base, int row, int col) {
   const int chunk = col >> 3;
-  const uint32_t off = (uint32_t)(row * 256 + 16 * (chunk ^ trs_swz(row)) + 8 * ((col >> 2) & 1));
+  const uint32_t off = (uint32_t)(row * 256 + 16 * (chunk ^ SW::f(row)) + 8 * ((col >> 2) & 1));
   typedef __attribute__((address_space(3))) s16x4* lptr;
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lptr)(base + off)));
 }
@@ -166,13 +181,19 @@ __device__ __forceinline__ u32x2 tr_read256(const char* base, int row, int col) 
 // K-contiguous MFMA A operand for MFMA row (lane % 32) of the 32-column block
 // starting at col0, rows k0 + 8 (lane / 32) + 0..7 of a swizzled 256-byte-row
 // tile (see tr_read256).
+template <class SW = TrSwz>
 __device__ __forceinline__ u32x4 tr_operand(const char* base, int k0, int col0, int lane) {
   const int g = lane >> 4, s = lane & 15;
   const int row = k0 + 8 * (g >> 1) + (s >> 2);
   const int col = col0 + 16 * (g & 1) + 4 * (s & 3);
-  const u32x2 lo = tr_read256(base, row, col);
-  const u32x2 hi = tr_read256(base, row + 4, col);
+  const u32x2 lo = tr_read256<SW>(base, row, col);
+  const u32x2 hi = tr_read256<SW>(base, row + 4, col);
   return u32x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// 16-byte chunk `chunk` of row `row` of a dual-swizzled 256-byte-row tile.
+__device__ __forceinline__ u32x4 dual_row_read(const char* base, int row, int chunk) {
+  return *(const u32x4*)(base + row * 256 + 16 * (chunk ^ dual_swz(row)));
 }
 
 __device__ __forceinline__ void wait_vmcnt0() {

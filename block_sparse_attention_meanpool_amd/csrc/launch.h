@@ -46,6 +46,20 @@ hipError_t launch_linear_prepare(const uint16_t* k, const uint16_t* v, int64_t B
 // O_lin (fp32) from a prepared workspace
 hipError_t launch_linear_apply(const uint16_t* q, int64_t BH, int N, int d, int block, int nb,
                                void* ws, float* o_lin, hipStream_t s);
+// Softmax-branch backward workspace: D (fp32 [BH, N]), the column bit matrix
+// (wc words per key tile), column counts and column lists (uint16, width nb),
+// each piece 256-byte aligned.
+struct AttnBwdWs {
+  int wc;
+  size_t d_bytes, bits_bytes, cnt_bytes, idx_bytes, total;
+};
+AttnBwdWs attn_bwd_ws_layout(int64_t BH, int N, int nb);
+// d = 128, block = 128 only; dq, dk, dv fp32, overwritten
+hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
+                           int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
+                           float scale, const void* o_s, int o_fp32, const float* lse,
+                           const uint16_t* d_o, float* dq, float* dk, float* dv, void* ws,
+                           hipStream_t s);
 hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,
                           int64_t n_elems, hipStream_t s);
 

@@ -212,6 +212,35 @@ sla_status sla_combine(const void* o_s, int32_t o_s_is_fp32, const float* o_lin,
                        int64_t n_elems, hipStream_t stream);
 
 /*
+ * Gradients of the softmax branch with the class map held fixed (SLA post,
+ * results: the method is trained with a short fine-tuning).  For the loss
+ * gradient dO of O_s (bf16), with P = softmax over each query block's
+ * critical keys recomputed from `lse`:
+ *   D_n = dO_n . O_s_n,  dS = P * (dO V^T - D),
+ *   dQ = scale dS K,  dK = scale dS^T Q,  dV = P^T dO,
+ * each key and value summing over every query block whose list holds its tile.
+ * bf16 MFMA products (P and dS rounded to bf16), fp32 accumulation.
+ *
+ * q, k, v, crit_idx, crit_cnt, kc_max, scale  as given to sla_sparse_attn_fwd;
+ *           the lists must hold no repeated entry (sla_block_mask writes none)
+ * o_s, lse  that call's outputs (o_s fp32 when o_s_is_fp32 != 0, else bf16)
+ * d_o       bf16 [B, H, N, d]                                   (in)
+ * dq, dk, dv  fp32 [B, H, N, d], overwritten                    (out)
+ * ws        device workspace of at least sla_sparse_attn_bwd_ws_bytes() bytes
+ * Supported: d = 128, block = 128 (SLA_ERR_UNSUPPORTED otherwise).
+ */
+sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                               int64_t H, int64_t N, int64_t d, int32_t block,
+                               const int32_t* crit_idx, const int32_t* crit_cnt, int32_t kc_max,
+                               float scale, const void* o_s, int32_t o_s_is_fp32, const float* lse,
+                               const uint16_t* d_o, float* dq, float* dk, float* dv, void* ws,
+                               size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for sla_sparse_attn_bwd: D (fp32 [B, H, N]) and the
+ * per-key-tile query-block lists.  0 for unsupported arguments. */
+size_t sla_sparse_attn_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block);
+
+/*
  * Dense softmax attention with the same kernel core: every key block is kept
  * for every query block.  A baseline for timing the sparse path against.
  */

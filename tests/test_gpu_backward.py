@@ -1,0 +1,98 @@
+"""GPU parity of the backward pass (class map held fixed) against the oracle's
+fp64 gradients (oracle/grad.py), through the C ABI.
+
+Bars.  A gradient entry is a sum of products in which one factor (P or dS)
+is rounded to bf16 (unit roundoff 2^-8, so at most 2^-9 relative after
+rounding to nearest) and everything else is exact bf16 input or fp32
+accumulation; the rounding errors are independent, so the sum's error is a
+few times 2^-9 of the magnitude of its terms.  The output bars (rel-L2 5e-3,
+max-abs 2e-2) are therefore kept, with the max-abs bar taken relative to the
+gradient's scale: |got - ref| <= 2e-2 * max(1, max |ref|), since dK and dV
+sum over every query that attends a key and grow with that count.
+"""
+
+from fractions import Fraction as F
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_meanpool_amd as sla
+from gpu_util import MAX_ABS, REL_L2, check_close, say, to_dev
+from oracle import grad as ograd
+from oracle import sla as osla
+from synth import generate
+from synth.configs import Spec
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16_bits(x):
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def _grad_close(got, want, what, rel_l2=REL_L2):
+    scale = max(1.0, float(np.abs(want).max()))
+    return check_close(got, want, what, max_abs=MAX_ABS * scale, rel_l2=rel_l2)
+
+
+def _mask(nb, H, seed, dense_frac=0.35):
+    g = np.random.default_rng(seed)
+    cls = np.where(g.random((1, H, nb, nb)) < dense_frac, osla.CRITICAL, osla.SKIP).astype(np.uint8)
+    cls[0, 0, 0] = osla.CRITICAL           # a row with every tile
+    cls[0, 0, 1] = osla.SKIP               # a row with none
+    cls[0, 1, 2, :] = osla.SKIP
+    cls[0, 1, 2, nb - 1] = osla.CRITICAL   # only the ragged last tile
+    cls[0, 1, :, 3] = osla.SKIP            # a key tile no query block uses
+    return cls
+
+
+def _run(spec, cls, o_fp32=True, seed=5):
+    data = generate(spec, repairs=None, threads=1)
+    g = np.random.default_rng(seed)
+    do_bits = _bf16_bits(g.standard_normal((spec.B, spec.H, spec.N, spec.d)).astype(np.float32))
+    q, k, v, d_o = (to_dev(x) for x in (data["q"], data["k"], data["v"], do_bits))
+    width = spec.nb
+    idx, cnt = osla.index_lists(cls, osla.CRITICAL, width)
+    idx_d, cnt_d = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    o_s, lse = sla.sla_sparse_attn_fwd(q, k, v, spec.block, idx_d, cnt_d, o_fp32=o_fp32,
+                                       want_lse=True)
+    dq, dk, dv = sla.sla_sparse_attn_bwd(q, k, v, spec.block, idx_d, cnt_d, o_s, lse, d_o)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = (osla.bf16_to_f64(x) for x in (data["q"], data["k"], data["v"], do_bits))
+    ref = ograd.backward(q64, k64, v64, cls, spec.block, do64, branches=("softmax",))
+    return (dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()), ref
+
+
+SPEC = Spec(301, "bwd_small", B=1, H=2, N=1000, d=128, block=128, kind="fourier",
+            grid=(10, 10, 10), mode="topk", keep=F(1, 2))
+
+
+@pytest.mark.parametrize("o_fp32", [True, False], ids=["o_s_fp32", "o_s_bf16"])
+def test_softmax_backward_small(o_fp32):
+    say(f"[backward] softmax branch, N=1000 (ragged), o_s fp32={o_fp32}")
+    cls = _mask(SPEC.nb, SPEC.H, 11)
+    got, ref = _run(SPEC, cls, o_fp32)
+    # With a bf16 O_s, D_n = dO_n . O_s_n carries that rounding too (up to
+    # 2^-9 sum |dO| |O| per row, entering every dS of the row): the rel-L2
+    # bar doubles for that variant.
+    rel = REL_L2 if o_fp32 else 2 * REL_L2
+    for a, b, n in zip(got, ref, ("dQ", "dK", "dV")):
+        _grad_close(a, b, n, rel_l2=rel)
+    # the key tile no query block uses and the row with no tile get exactly nothing
+    assert not got[1][0, 1, 3 * 128:4 * 128].any() and not got[2][0, 1, 3 * 128:4 * 128].any()
+    assert not got[0][0, 0, 128:256].any()
+
+
+def test_softmax_backward_selected_mask():
+    spec = Spec(302, "bwd_topk", B=1, H=3, N=4000, d=128, block=128, kind="fourier",
+                grid=(10, 20, 20), mode="topk", keep=F(1, 4))
+    say("[backward] softmax branch, N=4000, top-k map from the GPU classifier")
+    data = generate(spec, repairs=None, threads=1)
+    q, k = to_dev(data["q"]), to_dev(data["k"])
+    kc = osla.count_from_fraction(spec.keep, spec.nb)
+    cls = sla.sla_pool_classify(q, k, spec.block, "topk", kc).cpu().numpy()
+    got, ref = _run(spec, cls)
+    for a, b, n in zip(got, ref, ("dQ", "dK", "dV")):
+        _grad_close(a, b, n)
