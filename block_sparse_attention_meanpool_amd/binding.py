@@ -48,6 +48,9 @@ _SIGS = {
     "sla_sparse_attn_bwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _F, _P,
                                    _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sla_sparse_attn_bwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32]),
+    "sla_linear_branch_bwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _P, _P,
+                                     _SZ, _P, _P, _P, _P, _SZ, _P]),
+    "sla_linear_branch_bwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32]),
     "sla_dense_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _F, _P, _I32, _P, _P]),
     "sla_status_string": (ctypes.c_char_p, [_I32]),
     "sla_version": (_I32, []),
@@ -276,6 +279,26 @@ def sla_sparse_attn_bwd(q, k, v, block, crit_idx, crit_cnt, o_s, lse, d_o, scale
           _ptr(crit_cnt), crit_idx.shape[-1], float(scale), _ptr(o_s),
           int(o_s.dtype == torch.float32), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    return dq, dk, dv
+
+
+def sla_linear_branch_bwd(q, k, v, block, marg_idx, marg_cnt, d_o, lin_ws, dq, dk, dv, ws=None,
+                          stream=None):
+    """Adds the linear branch's gradients into dq, dk, dv (fp32)."""
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
+        _dev(t, torch.bfloat16, n)
+    _dev(marg_idx, torch.int32, "marg_idx")
+    _dev(marg_cnt, torch.int32, "marg_cnt")
+    _dev(lin_ws, torch.uint8, "lin_ws")
+    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _dev(t, torch.float32, n)
+    B, H, N, d = q.shape
+    need = lib().sla_linear_branch_bwd_ws_bytes(B, H, N, d, block)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _call("sla_linear_branch_bwd", _ptr(q), _ptr(k), _ptr(v), B, H, N, d, block, _ptr(marg_idx),
+          _ptr(marg_cnt), marg_idx.shape[-1], _ptr(d_o), _ptr(lin_ws), lin_ws.numel(), _ptr(dq),
+          _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     return dq, dk, dv
 
 

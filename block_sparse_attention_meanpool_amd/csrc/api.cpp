@@ -233,6 +233,39 @@ sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
                                        stream));
 }
 
+size_t sla_linear_branch_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {
+  int64_t nb = 0;
+  if (check_shape(B, H, N, d, block, &nb) != SLA_OK || d != 128 || block != 128) return 0;
+  return sla::linear_bwd_ws_layout(B * H, (int)nb).total;
+}
+
+sla_status sla_linear_branch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                                 int64_t H, int64_t N, int64_t d, int32_t block,
+                                 const int32_t* marg_idx, const int32_t* marg_cnt, int32_t km_max,
+                                 const uint16_t* d_o, const void* lin_ws, size_t lin_ws_bytes,
+                                 float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                                 hipStream_t stream) {
+  int64_t nb = 0;
+  sla_status st = check_shape(B, H, N, d, block, &nb);
+  if (st != SLA_OK) return st;
+  if (d != 128 || block != 128) return SLA_ERR_UNSUPPORTED;
+  if (!q || !k || !v || !marg_idx || !marg_cnt || !d_o || !dq || !dk || !dv)
+    return SLA_ERR_INVALID_ARG;
+  if (km_max < 1 || km_max > nb) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(d_o) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv))
+    return SLA_ERR_ALIGNMENT;
+  const int64_t BH = B * H;
+  if ((BH * nb * km_max + 255) / 256 > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
+  if (!lin_ws || lin_ws_bytes < sla_linear_branch_ws_bytes(B, H, N, d, block) ||
+      !aligned16(lin_ws))
+    return SLA_ERR_WORKSPACE;
+  const size_t need = sla_linear_branch_bwd_ws_bytes(B, H, N, d, block);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  return from_hip(sla::launch_linear_bwd(q, k, v, BH, (int)N, (int)nb, marg_idx, marg_cnt, km_max,
+                                         d_o, lin_ws, dq, dk, dv, ws, stream));
+}
+
 sla_status sla_combine(const void* o_s, int32_t o_s_is_fp32, const float* o_lin, uint16_t* o,
                        int64_t n_elems, hipStream_t stream) {
   if (!o_s || !o || n_elems < 0 || n_elems % 8 != 0) return SLA_ERR_INVALID_ARG;

@@ -391,6 +391,20 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(
 
 }  // namespace bwd
 
+hipError_t launch_col_bits(const int32_t* idx, const int32_t* cnt, int kmax, int64_t BH, int nrows,
+                           int ncols, int WC, uint32_t* bitsT, hipStream_t s) {
+  const int64_t nwords = BH * ncols * WC;
+  const int64_t fill_blocks = (nwords + 255) / 256;
+  bwd::fill_u32_kernel<<<dim3((unsigned)(fill_blocks < 65536 ? fill_blocks : 65536)), 256, 0, s>>>(
+      bitsT, nwords, 0u);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = BH * nrows;
+  bwd::col_bits_kernel<<<dim3((unsigned)((rows * kmax + 255) / 256)), 256, 0, s>>>(
+      idx, cnt, kmax, rows, nrows, ncols, WC, bitsT);
+  return hipGetLastError();
+}
+
 AttnBwdWs attn_bwd_ws_layout(int64_t BH, int N, int nb) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   AttnBwdWs w;
@@ -415,17 +429,9 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   int32_t* col_cnt = reinterpret_cast<int32_t*>(p + lw.d_bytes + lw.bits_bytes);
   uint16_t* col_idx = reinterpret_cast<uint16_t*>(p + lw.d_bytes + lw.bits_bytes + lw.cnt_bytes);
 
-  const int64_t nwords = BH * nb * lw.wc;
-  const int64_t fill_blocks = (nwords + 255) / 256;
-  bwd::fill_u32_kernel<<<dim3((unsigned)(fill_blocks < 65536 ? fill_blocks : 65536)), 256, 0, s>>>(
-      bitsT, nwords, 0u);
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_col_bits(idx, cnt, kmax, BH, nb, nb, lw.wc, bitsT, s);
   if (e != hipSuccess) return e;
   const int64_t rows = BH * nb;
-  bwd::col_bits_kernel<<<dim3((unsigned)((rows * kmax + 255) / 256)), 256, 0, s>>>(
-      idx, cnt, kmax, rows, nb, nb, lw.wc, bitsT);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
   bwd::col_lists_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(bitsT, rows, lw.wc, nb,
                                                                           col_idx, col_cnt);
   e = hipGetLastError();

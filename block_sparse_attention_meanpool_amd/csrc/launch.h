@@ -43,6 +43,18 @@ LinearPtrs linear_ws_ptrs(void* ws, int64_t BH, int nb, int d);
 hipError_t launch_linear_prepare(const uint16_t* k, const uint16_t* v, int64_t BH, int N, int d,
                                  int block, int nb, const int32_t* idx, const int32_t* cnt,
                                  int kmax, void* ws, hipStream_t s);
+// C[row] = sum over the set bits k of bit row `row` of Ht[k] (rows of d*d bf16),
+// per head: the masked-GEMM gather (nb bit rows of W words, nb source rows)
+hipError_t launch_gather(const uint16_t* Ht, const uint32_t* bits, int64_t BH, int nb, int W, int d,
+                         uint16_t* C, hipStream_t s);
+// out[row] = sum of src rows (fp32 [nsrc, d] per head) over the set bits of
+// bit row `row`, in ascending order; per_head bit rows per head
+hipError_t launch_bitrow_sums(const uint32_t* bits, int W, int64_t rows, int per_head, int nsrc,
+                              const float* src, float* out, int d, hipStream_t s);
+// Column bit matrix of per-row index lists: bit (j, i) for every entry j of
+// row i (entries outside [0, ncols) dropped); clears the matrix first
+hipError_t launch_col_bits(const int32_t* idx, const int32_t* cnt, int kmax, int64_t BH, int nrows,
+                           int ncols, int WC, uint32_t* bitsT, hipStream_t s);
 // O_lin (fp32) from a prepared workspace
 hipError_t launch_linear_apply(const uint16_t* q, int64_t BH, int N, int d, int block, int nb,
                                void* ws, float* o_lin, hipStream_t s);
@@ -60,6 +72,19 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            float scale, const void* o_s, int o_fp32, const float* lse,
                            const uint16_t* d_o, float* dq, float* dk, float* dv, void* ws,
                            hipStream_t s);
+// Linear-branch backward workspace: dS_i (bf16, laid out like the states),
+// dzeta_i (fp32), the transposed marginal bit matrix, dH_j (bf16), dz_j (fp32).
+struct LinearBwdWs {
+  int words;
+  size_t ds_bytes, dzeta_bytes, bits_bytes, dh_bytes, dz_bytes, total;
+};
+LinearBwdWs linear_bwd_ws_layout(int64_t BH, int nb);
+// d = 128, block = 128 only; lin_ws prepared by launch_linear_prepare for the
+// same inputs; dq, dk, dv fp32, accumulated into
+hipError_t launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
+                             int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
+                             const uint16_t* d_o, const void* lin_ws, float* dq, float* dk,
+                             float* dv, void* ws, hipStream_t s);
 hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,
                           int64_t n_elems, hipStream_t s);
 

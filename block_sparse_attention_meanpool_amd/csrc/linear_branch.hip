@@ -110,38 +110,17 @@ __global__ __launch_bounds__(256) void lin_state_kernel(const uint16_t* __restri
   }
 }
 
-// Marginal list of each query block -> a row of the bit matrix (W 32-bit
-// words, W even, W <= 128) and zeta_i = sum of z_j over the set bits in
-// ascending j (fp32).  One wave per row; entries outside [0, nkb) are dropped
-// and a repeated entry counts once, as it does in the bit row.
+// Sum of the rows src[j] (fp32, D features) over the set bits j of a bit row
+// held in LDS (W <= 128 words), strictly in ascending j: the set bits are
+// compacted into a list first (popcount prefix over the lanes), then summed
+// with 8 loads in flight.  One wave; each lane owns D / 64 features.
 template <int D>
-__global__ __launch_bounds__(256) void lin_mask_kernel(const int32_t* __restrict__ idx,
-                                                       const int32_t* __restrict__ cnt, int kmax,
-                                                       int64_t rows, int nqb, int nkb, int W,
-                                                       const float* __restrict__ Zs,
-                                                       uint32_t* __restrict__ bits,
-                                                       float* __restrict__ zeta) {
-  constexpr int PER = D / 64;  // features per lane
-  __shared__ uint32_t words[4][128];
-  __shared__ uint16_t js[4][4096];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
-  if (row >= rows) return;
-  for (int x = lane; x < W; x += 64) words[wv][x] = 0u;
-  __builtin_amdgcn_wave_barrier();
-  const int c = min(cnt[row], kmax);
-  const int32_t* list = idx + row * kmax;
-  for (int t = lane; t < c; t += 64) {
-    const int j = list[t];
-    if (j >= 0 && j < nkb) atomicOr(&words[wv][j >> 5], 1u << (j & 31));
-  }
-  __builtin_amdgcn_wave_barrier();
-
-  // bit row out; the set bits compacted to an ascending list of j in LDS
-  uint32_t w0 = lane < W ? words[wv][lane] : 0u;
-  uint32_t w1 = lane + 64 < W ? words[wv][lane + 64] : 0u;
-  if (lane < W) bits[row * W + lane] = w0;
-  if (lane + 64 < W) bits[row * W + lane + 64] = w1;
+__device__ __forceinline__ void bitrow_sum(const uint32_t* words, int W, uint16_t* js,
+                                           const float* __restrict__ src, float* __restrict__ out,
+                                           int lane) {
+  constexpr int PER = D / 64;
+  uint32_t w0 = lane < W ? words[lane] : 0u;
+  uint32_t w1 = lane + 64 < W ? words[lane + 64] : 0u;
   const int c0 = __popc(w0), c1 = __popc(w1);
   int s0 = c0, s1 = c1;  // inclusive prefix sums over lanes
 #pragma unroll
@@ -156,17 +135,15 @@ __global__ __launch_bounds__(256) void lin_mask_kernel(const int32_t* __restrict
   const int total = tot0 + __shfl(s1, 63);
   int p0 = s0 - c0, p1 = tot0 + s1 - c1;
   while (w0) {
-    js[wv][p0++] = (uint16_t)(32 * lane + __ffs(w0) - 1);
+    js[p0++] = (uint16_t)(32 * lane + __ffs(w0) - 1);
     w0 &= w0 - 1u;
   }
   while (w1) {
-    js[wv][p1++] = (uint16_t)(32 * (lane + 64) + __ffs(w1) - 1);
+    js[p1++] = (uint16_t)(32 * (lane + 64) + __ffs(w1) - 1);
     w1 &= w1 - 1u;
   }
   __builtin_amdgcn_wave_barrier();
-
-  // zeta_i: 8 loads in flight, added strictly in list order
-  const float* zb = Zs + (row / nqb) * (int64_t)nkb * D + PER * lane;
+  const float* sb = src + PER * lane;
   float acc[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) acc[e] = 0.f;
@@ -174,9 +151,9 @@ __global__ __launch_bounds__(256) void lin_mask_kernel(const int32_t* __restrict
     float val[8][PER];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int j = js[wv][min(t + u, total - 1)];
+      const int j = js[min(t + u, total - 1)];
 #pragma unroll
-      for (int e = 0; e < PER; ++e) val[u][e] = zb[j * D + e];
+      for (int e = 0; e < PER; ++e) val[u][e] = sb[j * D + e];
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u)
@@ -184,7 +161,54 @@ __global__ __launch_bounds__(256) void lin_mask_kernel(const int32_t* __restrict
       for (int e = 0; e < PER; ++e) acc[e] += t + u < total ? val[u][e] : 0.f;
   }
 #pragma unroll
-  for (int e = 0; e < PER; ++e) zeta[row * D + PER * lane + e] = acc[e];
+  for (int e = 0; e < PER; ++e) out[PER * lane + e] = acc[e];
+}
+
+// Marginal list of each query block -> a row of the bit matrix (W 32-bit
+// words, W even, W <= 128) and zeta_i = sum of z_j over the set bits in
+// ascending j (fp32).  One wave per row; entries outside [0, nkb) are dropped
+// and a repeated entry counts once, as it does in the bit row.
+template <int D>
+__global__ __launch_bounds__(256) void lin_mask_kernel(const int32_t* __restrict__ idx,
+                                                       const int32_t* __restrict__ cnt, int kmax,
+                                                       int64_t rows, int nqb, int nkb, int W,
+                                                       const float* __restrict__ Zs,
+                                                       uint32_t* __restrict__ bits,
+                                                       float* __restrict__ zeta) {
+  __shared__ uint32_t words[4][128];
+  __shared__ uint16_t js[4][4096];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
+  if (row >= rows) return;
+  for (int x = lane; x < W; x += 64) words[wv][x] = 0u;
+  __builtin_amdgcn_wave_barrier();
+  const int c = min(cnt[row], kmax);
+  const int32_t* list = idx + row * kmax;
+  for (int t = lane; t < c; t += 64) {
+    const int j = list[t];
+    if (j >= 0 && j < nkb) atomicOr(&words[wv][j >> 5], 1u << (j & 31));
+  }
+  __builtin_amdgcn_wave_barrier();
+  for (int x = lane; x < W; x += 64) bits[row * W + x] = words[wv][x];
+  bitrow_sum<D>(words[wv], W, js[wv], Zs + (row / nqb) * (int64_t)nkb * D, zeta + row * D, lane);
+}
+
+// out[row] = sum of src rows over the set bits of bit row `row` (ascending),
+// for bit rows already in memory; src holds nsrc rows per head.
+template <int D>
+__global__ __launch_bounds__(256) void lin_bitrow_sum_kernel(const uint32_t* __restrict__ bits,
+                                                             int W, int64_t rows, int per_head,
+                                                             int nsrc, const float* __restrict__ src,
+                                                             float* __restrict__ out) {
+  __shared__ uint32_t words[4][128];
+  __shared__ uint16_t js[4][4096];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
+  if (row >= rows) return;
+  for (int x = lane; x < W; x += 64) words[wv][x] = bits[row * W + x];
+  __builtin_amdgcn_wave_barrier();
+  bitrow_sum<D>(words[wv], W, js[wv], src + (row / per_head) * (int64_t)nsrc * D, out + row * D,
+                lane);
 }
 
 // 8 mask bits -> 8 bf16 values 1.0 / 0.0 (the B operand of the gather GEMM).
@@ -397,12 +421,31 @@ static hipError_t launch_linear_prepare_t(const uint16_t* k, const uint16_t* v, 
                                                                       lp.zeta);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rowtiles = (nb + 127) / 128, coltiles = D * D / 128;
+  return launch_gather(lp.Ht, lp.bits, BH, nb, lp.words, D, lp.C, s);
+}
+
+hipError_t launch_gather(const uint16_t* Ht, const uint32_t* bits, int64_t BH, int nb, int W, int d,
+                         uint16_t* C, hipStream_t s) {
+  const int rowtiles = (nb + 127) / 128, coltiles = d * d / 128;
   const int64_t tiles = BH * rowtiles * coltiles;
   const int per_xcd = (int)((tiles + 7) / 8);
-  const size_t mbytes = (size_t)128 * (lp.words + 1) * sizeof(uint32_t);
-  lin_gather_kernel<D><<<dim3((unsigned)(per_xcd * 8)), 256, mbytes, s>>>(
-      lp.Ht, lp.bits, nb, nb, lp.words, rowtiles, coltiles, per_xcd, tiles, lp.C);
+  const size_t mbytes = (size_t)128 * (W + 1) * sizeof(uint32_t);
+  if (d == 128)
+    lin_gather_kernel<128><<<dim3((unsigned)(per_xcd * 8)), 256, mbytes, s>>>(
+        Ht, bits, nb, nb, W, rowtiles, coltiles, per_xcd, tiles, C);
+  else
+    lin_gather_kernel<64><<<dim3((unsigned)(per_xcd * 8)), 256, mbytes, s>>>(
+        Ht, bits, nb, nb, W, rowtiles, coltiles, per_xcd, tiles, C);
+  return hipGetLastError();
+}
+
+hipError_t launch_bitrow_sums(const uint32_t* bits, int W, int64_t rows, int per_head, int nsrc,
+                              const float* src, float* out, int d, hipStream_t s) {
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (d == 128)
+    lin_bitrow_sum_kernel<128><<<grid, 256, 0, s>>>(bits, W, rows, per_head, nsrc, src, out);
+  else
+    lin_bitrow_sum_kernel<64><<<grid, 256, 0, s>>>(bits, W, rows, per_head, nsrc, src, out);
   return hipGetLastError();
 }
 

@@ -1,0 +1,291 @@
+// Backward pass of the linear-attention branch with the class map held fixed
+// (SLA post: intermediate blocks via linear attention, phi = elu + 1; results:
+// the method is trainable).  With a = phi(q), S_i, zeta_i from the forward's
+// prepared workspace, w_n = a_n . zeta_i and O_lin_n = a_n^T S_i / w_n:
+//   g_n = dO_n / w_n,  h_n = -(dO_n . O_lin_n) / w_n
+//   dq_n  += (S_i g_n + zeta_i h_n) * phi'(q_n)
+//   dS_i   = A_i^T G_i,  dzeta_i = A_i^T h          (query side, per block)
+//   dH_j   = sum over i with j in marg_i of dS_i,  dz_j likewise
+//                                                   (the transposed mask GEMM)
+//   dk_m  += (dH_j v_m + dz_j) * phi'(k_m),  dv_m += dH_j^T phi(k_m)
+//                                                   (key side, per tile)
+// d = 128, 128-token blocks; dq, dk, dv are fp32 and accumulated into.
+#include "common.h"
+#include "launch.h"
+#include "linear_apply.h"
+
+namespace sla {
+namespace lbwd {
+
+constexpr int D = 128, BLK = 128, NT = 256;
+
+__device__ __forceinline__ float dphi(float x) { return x > 0.f ? 1.f : __expf(x); }
+
+// 32 KB row-major tile (128 rows of 256 bytes) from global into dual-swizzled
+// LDS by asynchronous LDS-direct loads: 8 instructions of 1 KB per wave.
+__device__ __forceinline__ void stage_tile(const uint16_t* src, char* dst, int lane, int w) {
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(src, D * D * 2);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int inst = 8 * w + e;
+    const int row = 4 * inst + (lane >> 4);
+    const int ch = (lane & 15) ^ dual_swz(row);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_ptr)(dst + inst * 1024), 16,
+                                             (uint32_t)(row * D + ch * 8) * 2, 0, 0, 0);
+  }
+}
+
+__device__ __forceinline__ char* row_chunk(char* base, int row, int chunk) {
+  return base + row * 256 + 16 * (chunk ^ dual_swz(row));
+}
+
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+// One workgroup per query block, 4 waves of 32 queries.
+__global__ __launch_bounds__(NT) void lin_bwd_query_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ d_o, int N, int nqb,
+    const uint16_t* __restrict__ C, const float* __restrict__ zeta, float* __restrict__ dq,
+    uint16_t* __restrict__ dS, float* __restrict__ dzeta) {
+  __shared__ __attribute__((aligned(1024))) char SB[D * 256];    // S_i^T rows e, then G rows n
+  __shared__ __attribute__((aligned(1024))) char AB[BLK * 256];  // phi(Q) rows n
+  __shared__ float hs[BLK];
+  const int64_t bh = blockIdx.x / nqb;
+  const int qb = blockIdx.x % nqb;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int64_t head_off = bh * (int64_t)N * D;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(d_o + head_off, (uint32_t)N * D * 2);
+  const int64_t row = bh * nqb + qb;
+  const uint16_t* St = C + row * D * D;
+  const float* zt = zeta + row * D;
+  stage_tile(St, SB, lane, w);
+
+  const int n = 32 * w + l32;  // query within the block
+  const int qrow = qb * BLK + n;
+  u32x4 qf[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) qf[ks] = buf_load16(rq, (uint32_t)(qrow * D + 16 * ks + 8 * hf) * 2);
+  float linv;
+  float hdot = 0.f;
+  {
+    f32x16 acc[4];
+    linv = linear_apply<D>(St, zt, qf, l32, hf, acc);  // acc * linv = O_lin^T
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const u32x2 x = buf_load8(rdo, (uint32_t)(qrow * D + 32 * db + 8 * g + 4 * hf) * 2);
+        hdot = fmaf(bf16_bits_to_f32(x[0] & 0xffffu), acc[db][4 * g], hdot);
+        hdot = fmaf(bf16_bits_to_f32(x[0] >> 16), acc[db][4 * g + 1], hdot);
+        hdot = fmaf(bf16_bits_to_f32(x[1] & 0xffffu), acc[db][4 * g + 2], hdot);
+        hdot = fmaf(bf16_bits_to_f32(x[1] >> 16), acc[db][4 * g + 3], hdot);
+      }
+  }
+  hdot = sum_halves(hdot);
+  const float hn = -hdot * linv * linv;  // -(dO . O_lin) / w
+  // g_n = dO_n / w_n as the B operand (bf16); phi(q_n) rows into LDS
+  u32x4 gb[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const u32x4 x = buf_load16(rdo, (uint32_t)(qrow * D + 16 * ks + 8 * hf) * 2);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      gb[ks][e] = pack_bf16x2(bf16_bits_to_f32(x[e] & 0xffffu) * linv,
+                              bf16_bits_to_f32(x[e] >> 16) * linv);
+    *(u32x4*)row_chunk(AB, n, 2 * ks + hf) = phi8(qf[ks], true);
+  }
+  if (hf == 0) hs[n] = hn;
+  wait_vmcnt0();
+  __syncthreads();  // S_i^T staged; phi(Q) rows and h written
+
+  // da^T = S_i G^T: A = S_i [c x e] by transposed reads of the S_i^T rows
+  {
+    f32x16 dacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+        dacc[cb] = mfma32x32x16(tr_operand<DualSwz>(SB, 16 * ks, 32 * cb, lane), gb[ks], dacc[cb]);
+    if (qrow < N) {
+      float* drow = dq + head_off + (int64_t)qrow * D;
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int c0 = 32 * cb + 8 * g + 4 * hf;
+          const u32x2 x = buf_load8(rq, (uint32_t)(qrow * D + c0) * 2);
+          const f32x4 z4 = *(const f32x4*)(zt + c0);
+          const float qv[4] = {bf16_bits_to_f32(x[0] & 0xffffu), bf16_bits_to_f32(x[0] >> 16),
+                               bf16_bits_to_f32(x[1] & 0xffffu), bf16_bits_to_f32(x[1] >> 16)};
+          f32x4 cur = *(f32x4*)(drow + c0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) cur[r] += fmaf(z4[r], hn, dacc[cb][4 * g + r]) * dphi(qv[r]);
+          *(f32x4*)(drow + c0) = cur;
+        }
+    }
+  }
+  __syncthreads();  // every wave is done reading S_i^T
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) *(u32x4*)row_chunk(SB, n, 2 * ks + hf) = gb[ks];
+  __syncthreads();
+
+  // dS_i [c x e] = A^T G over the block's queries: 16 blocks of 32 x 32, 4 per wave
+  f32x16 sacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int cb = w, eb = u;
+      sacc[u] = mfma32x32x16(tr_operand<DualSwz>(AB, 16 * ks, 32 * cb, lane),
+                             tr_operand<DualSwz>(SB, 16 * ks, 32 * eb, lane), sacc[u]);
+    }
+  // stored like the forward states: dS[row][e * D + c]
+  uint16_t* dSi = dS + row * D * D;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int e = 32 * u + l32;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int c = 32 * w + 8 * g + 4 * hf;
+      *(u32x2*)(dSi + e * D + c) = u32x2{pack_bf16x2(sacc[u][4 * g], sacc[u][4 * g + 1]),
+                                         pack_bf16x2(sacc[u][4 * g + 2], sacc[u][4 * g + 3])};
+    }
+  }
+  // dzeta_i[c] = sum_n a_n[c] h_n, in query order
+  if (tid < D) {
+    float z = 0.f;
+    for (int m = 0; m < BLK; ++m) {
+      const uint16_t a = *(const uint16_t*)(row_chunk(AB, m, tid >> 3) + 2 * (tid & 7));
+      z = fmaf(bf16_bits_to_f32(a), hs[m], z);
+    }
+    dzeta[row * D + tid] = z;
+  }
+}
+
+// One workgroup per key tile, 4 waves of 32 keys (one key per lane).
+__global__ __launch_bounds__(NT) void lin_bwd_key_kernel(const uint16_t* __restrict__ k,
+                                                         const uint16_t* __restrict__ v, int N,
+                                                         int nkb, const uint16_t* __restrict__ dHt,
+                                                         const float* __restrict__ dz,
+                                                         float* __restrict__ dk,
+                                                         float* __restrict__ dv) {
+  __shared__ __attribute__((aligned(1024))) char HB[D * 256];  // dH_j^T rows e
+  const int64_t bh = blockIdx.x / nkb;
+  const int j = blockIdx.x % nkb;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int64_t head_off = bh * (int64_t)N * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, (uint32_t)N * D * 2);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, (uint32_t)N * D * 2);
+  const int64_t row = bh * nkb + j;
+  stage_tile(dHt + row * D * D, HB, lane, w);
+  const int key = j * BLK + 32 * w + l32;
+  u32x4 vf[8], pk[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    const uint32_t off = (uint32_t)(key * D + 16 * ks + 8 * hf) * 2;
+    vf[ks] = buf_load16(rv, off);
+    pk[ks] = phi8(buf_load16(rk, off), key < N);
+  }
+  wait_vmcnt0();
+  __syncthreads();
+
+  // dPhi^T [c x m] = dH_j [c x e] V^T: A by transposed reads of dH_j^T rows e
+  f32x16 pacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+      pacc[cb] = mfma32x32x16(tr_operand<DualSwz>(HB, 16 * ks, 32 * cb, lane), vf[ks], pacc[cb]);
+  if (key < N) {
+    float* krow = dk + head_off + (int64_t)key * D;
+    const float* zr = dz + row * D;
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c0 = 32 * cb + 8 * g + 4 * hf;
+        const u32x2 x = buf_load8(rk, (uint32_t)(key * D + c0) * 2);
+        const f32x4 z4 = *(const f32x4*)(zr + c0);
+        const float kv[4] = {bf16_bits_to_f32(x[0] & 0xffffu), bf16_bits_to_f32(x[0] >> 16),
+                             bf16_bits_to_f32(x[1] & 0xffffu), bf16_bits_to_f32(x[1] >> 16)};
+        f32x4 cur = *(f32x4*)(krow + c0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cur[r] += (pacc[cb][4 * g + r] + z4[r]) * dphi(kv[r]);
+        *(f32x4*)(krow + c0) = cur;
+      }
+  }
+  // dV^T [e x m] = dH_j^T [e x c] Phi^T: A by row reads of dH_j^T
+  f32x16 vacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+    for (int eb = 0; eb < 4; ++eb)
+      vacc[eb] = mfma32x32x16(dual_row_read(HB, 32 * eb + l32, 2 * ks + hf), pk[ks], vacc[eb]);
+  if (key < N) {
+    float* vrow = dv + head_off + (int64_t)key * D;
+#pragma unroll
+    for (int eb = 0; eb < 4; ++eb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int e0 = 32 * eb + 8 * g + 4 * hf;
+        f32x4 cur = *(f32x4*)(vrow + e0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cur[r] += vacc[eb][4 * g + r];
+        *(f32x4*)(vrow + e0) = cur;
+      }
+  }
+}
+
+}  // namespace lbwd
+
+LinearBwdWs linear_bwd_ws_layout(int64_t BH, int nb) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  constexpr int D = lbwd::D;
+  LinearBwdWs w;
+  w.words = 2 * ((nb + 63) / 64);
+  w.ds_bytes = up((size_t)BH * nb * D * D * 2);
+  w.dzeta_bytes = up((size_t)BH * nb * D * 4);
+  w.bits_bytes = up((size_t)BH * nb * w.words * 4);
+  w.dh_bytes = up((size_t)BH * nb * D * D * 2);
+  w.dz_bytes = up((size_t)BH * nb * D * 4);
+  w.total = w.ds_bytes + w.dzeta_bytes + w.bits_bytes + w.dh_bytes + w.dz_bytes;
+  return w;
+}
+
+hipError_t launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
+                             int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
+                             const uint16_t* d_o, const void* lin_ws, float* dq, float* dk,
+                             float* dv, void* ws, hipStream_t s) {
+  constexpr int D = lbwd::D;
+  const LinearPtrs lp = linear_ws_ptrs(const_cast<void*>(lin_ws), BH, nb, D);
+  const LinearBwdWs lw = linear_bwd_ws_layout(BH, nb);
+  char* p = static_cast<char*>(ws);
+  uint16_t* dS = reinterpret_cast<uint16_t*>(p);
+  p += lw.ds_bytes;
+  float* dzeta = reinterpret_cast<float*>(p);
+  p += lw.dzeta_bytes;
+  uint32_t* bitsT = reinterpret_cast<uint32_t*>(p);
+  p += lw.bits_bytes;
+  uint16_t* dH = reinterpret_cast<uint16_t*>(p);
+  p += lw.dh_bytes;
+  float* dz = reinterpret_cast<float*>(p);
+
+  const dim3 grid((unsigned)(BH * nb));
+  lbwd::lin_bwd_query_kernel<<<grid, lbwd::NT, 0, s>>>(q, d_o, N, nb, lp.C, lp.zeta, dq, dS, dzeta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  e = launch_col_bits(idx, cnt, kmax, BH, nb, nb, lw.words, bitsT, s);
+  if (e != hipSuccess) return e;
+  e = launch_gather(dS, bitsT, BH, nb, lw.words, D, dH, s);
+  if (e != hipSuccess) return e;
+  e = launch_bitrow_sums(bitsT, lw.words, BH * nb, nb, nb, dzeta, dz, D, s);
+  if (e != hipSuccess) return e;
+  lbwd::lin_bwd_key_kernel<<<grid, lbwd::NT, 0, s>>>(k, v, N, nb, dH, dz, dk, dv);
+  return hipGetLastError();
+}
+
+}  // namespace sla

@@ -241,6 +241,39 @@ sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
 size_t sla_sparse_attn_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block);
 
 /*
+ * Gradients of the linear branch with the class map held fixed (SLA post:
+ * intermediate blocks via linear attention; results: trainable).  With
+ * a = phi(q), w_n = a_n . zeta_i and O_lin_n = a_n^T S_i / w_n, for the loss
+ * gradient dO of O_lin (bf16):
+ *   g_n = dO_n / w_n,  h_n = -(dO_n . O_lin_n) / w_n,
+ *   dQ_n += (S_i g_n + zeta_i h_n) * phi'(q_n),
+ *   dS_i = sum_n a_n g_n^T,  dzeta_i = sum_n a_n h_n,
+ *   dH_j = sum of dS_i over the query blocks i whose marginal list holds j,
+ *   dz_j likewise,
+ *   dK_m += (dH_j v_m + dz_j) * phi'(k_m),  dV_m += dH_j^T phi(k_m),
+ * with phi'(x) = 1 for x > 0 and exp(x) otherwise.  phi(q), phi(k), g and
+ * the states enter bf16 MFMA products; sums are fp32.
+ *
+ * q, k, v, marg_idx, marg_cnt, km_max  as given to the forward
+ * d_o       bf16 [B, H, N, d]                                   (in)
+ * lin_ws    the workspace that sla_linear_branch_prepare (or
+ *           sla_linear_branch_fwd) filled for the same q, k, v and lists (in)
+ * dq, dk, dv  fp32 [B, H, N, d]: the gradients are ADDED to their contents,
+ *           so a call after sla_sparse_attn_bwd yields both branches' sum
+ * ws        device workspace of at least sla_linear_branch_bwd_ws_bytes() bytes
+ * Supported: d = 128, block = 128 (SLA_ERR_UNSUPPORTED otherwise).
+ */
+sla_status sla_linear_branch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
+                                 int64_t H, int64_t N, int64_t d, int32_t block,
+                                 const int32_t* marg_idx, const int32_t* marg_cnt, int32_t km_max,
+                                 const uint16_t* d_o, const void* lin_ws, size_t lin_ws_bytes,
+                                 float* dq, float* dk, float* dv, void* ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* Workspace bytes for sla_linear_branch_bwd.  0 for unsupported arguments. */
+size_t sla_linear_branch_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block);
+
+/*
  * Dense softmax attention with the same kernel core: every key block is kept
  * for every query block.  A baseline for timing the sparse path against.
  */

@@ -96,3 +96,61 @@ def test_softmax_backward_selected_mask():
     got, ref = _run(spec, cls)
     for a, b, n in zip(got, ref, ("dQ", "dK", "dV")):
         _grad_close(a, b, n)
+
+
+def _mask3(nb, H, seed):
+    g = np.random.default_rng(seed)
+    cls = g.choice(np.array([osla.SKIP, osla.MARGINAL, osla.CRITICAL], dtype=np.uint8),
+                   size=(1, H, nb, nb), p=[0.4, 0.35, 0.25])
+    cls[0, 0, 0] = osla.MARGINAL           # every tile marginal
+    cls[0, 0, 1] = osla.SKIP               # nothing at all
+    cls[0, 1, 2, :] = osla.SKIP
+    cls[0, 1, 2, nb - 1] = osla.MARGINAL   # only the ragged last tile, marginal
+    cls[0, 1, 3, :] = osla.CRITICAL        # no marginal tile at all
+    cls[0, 1, :, 4] = osla.SKIP            # a key tile no query block uses
+    return cls
+
+
+def _run_both(spec, cls, branches, seed=9):
+    data = generate(spec, repairs=None, threads=1)
+    g = np.random.default_rng(seed)
+    do_bits = _bf16_bits(g.standard_normal((spec.B, spec.H, spec.N, spec.d)).astype(np.float32))
+    q, k, v, d_o = (to_dev(x) for x in (data["q"], data["k"], data["v"], do_bits))
+    nb, b = spec.nb, spec.block
+    ci, cc = (torch.from_numpy(x).cuda() for x in osla.index_lists(cls, osla.CRITICAL, nb))
+    mi, mc = (torch.from_numpy(x).cuda() for x in osla.index_lists(cls, osla.MARGINAL, nb))
+    if "softmax" in branches:
+        o_s, lse = sla.sla_sparse_attn_fwd(q, k, v, b, ci, cc, o_fp32=True, want_lse=True)
+        dq, dk, dv = sla.sla_sparse_attn_bwd(q, k, v, b, ci, cc, o_s, lse, d_o)
+    else:
+        dq, dk, dv = (torch.zeros(q.shape, dtype=torch.float32, device="cuda") for _ in range(3))
+    lin_ws = sla.sla_linear_branch_prepare(k, v, b, mi, mc)
+    sla.sla_linear_branch_bwd(q, k, v, b, mi, mc, d_o, lin_ws, dq, dk, dv)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = (osla.bf16_to_f64(x) for x in (data["q"], data["k"], data["v"], do_bits))
+    ref = ograd.backward(q64, k64, v64, cls, b, do64, branches=branches)
+    return (dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()), ref
+
+
+def test_linear_backward_small():
+    say("[backward] linear branch alone, N=1000 (ragged)")
+    cls = _mask3(SPEC.nb, SPEC.H, 21)
+    got, ref = _run_both(SPEC, cls, ("linear",))
+    # The linear branch's dQ is (S_i - zeta_i O_lin^T) g: two terms that largely
+    # cancel, each carrying the bf16 rounding of S_i (2^-9 relative), so its
+    # relative error is 2^-9 times the cancellation factor: its rel-L2 bar is
+    # doubled.  dK and dV have no such difference.
+    for a, b, n, rel in zip(got, ref, ("dQ", "dK", "dV"), (2 * REL_L2, REL_L2, REL_L2)):
+        _grad_close(a, b, n, rel_l2=rel)
+    assert not got[1][0, 1, 4 * 128:5 * 128].any() and not got[2][0, 1, 4 * 128:5 * 128].any()
+    assert not got[0][0, 0, 128:256].any() and not got[0][0, 1, 3 * 128:4 * 128].any()
+
+
+def test_both_branches_backward():
+    spec = Spec(303, "bwd_sla3", B=1, H=2, N=2900, d=128, block=128, kind="fourier",
+                grid=(10, 10, 29), mode="topk", keep=F(1, 2))
+    say("[backward] both branches, N=2900 (ragged), sparse then linear accumulating")
+    cls = _mask3(spec.nb, spec.H, 22)
+    got, ref = _run_both(spec, cls, ("softmax", "linear"))
+    for a, b, n in zip(got, ref, ("dQ", "dK", "dV")):
+        _grad_close(a, b, n)
