@@ -99,6 +99,59 @@ def measured_traffic(config_name):
         return None
 
 
+def backward_timing(sla, torch, q, k, v, b, crit_idx, crit_cnt, marg_idx, marg_cnt, km, flop,
+                    steps, stream):
+    """Gradients of the whole layer (mask held fixed) for a seeded dO: the
+    softmax branch's backward and, with marginal tiles, the linear branch's,
+    each timed with HIP events on the launch stream.  The forward's O_s and
+    LSE are computed first, outside the timed region."""
+    g = torch.Generator(device=q.device).manual_seed(7)
+    d_o = torch.randn(q.shape, generator=g, device=q.device, dtype=torch.float32).to(torch.bfloat16)
+    o_s, lse = sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt, o_fp32=False,
+                                       want_lse=True)
+    dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
+    B, H, N, d = q.shape
+    ws = torch.empty(sla.lib().sla_sparse_attn_bwd_ws_bytes(B, H, N, d, b), dtype=torch.uint8,
+                     device=q.device)
+    lin_ws = lws = None
+    if km:
+        lin_ws = sla.sla_linear_branch_prepare(k, v, b, marg_idx, marg_cnt)
+        lws = torch.empty(sla.lib().sla_linear_branch_bwd_ws_bytes(B, H, N, d, b),
+                          dtype=torch.uint8, device=q.device)
+
+    def run(marks):
+        if marks:
+            marks[0].record(stream)
+        sla.sla_sparse_attn_bwd(q, k, v, b, crit_idx, crit_cnt, o_s, lse, d_o, dq=dq, dk=dk, dv=dv,
+                                ws=ws)
+        if marks:
+            marks[1].record(stream)
+        if km:
+            sla.sla_linear_branch_bwd(q, k, v, b, marg_idx, marg_cnt, d_o, lin_ws, dq, dk, dv,
+                                      ws=lws)
+            if marks:
+                marks[2].record(stream)
+
+    run(None)
+    torch.cuda.synchronize()
+    reps = max(1, min(steps, 5))
+    all_marks = []
+    for _ in range(reps):
+        marks = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        run(marks)
+        all_marks.append(marks)
+    torch.cuda.synchronize()
+    sm = float(np.mean([m[0].elapsed_time(m[1]) for m in all_marks]))
+    out = {"sparse_bwd_ms": sm, "reps": reps,
+           "sparse_bwd_tflops_2p5x": 2.5 * flop / (sm * 1e-3) / 1e12,
+           "note": "2.5 x the kept forward FLOP, the usual accounting of an attention backward; "
+                   "the kernels recompute S and dP in both passes (3.5 x executed)"}
+    if km:
+        out["linear_bwd_ms"] = float(np.mean([m[1].elapsed_time(m[2]) for m in all_marks]))
+    del d_o, o_s, lse, dq, dk, dv, ws, lin_ws, lws
+    return out
+
+
 def describe(spec, kc, km):
     grid = f" ({'x'.join(str(x) for x in spec.grid)})" if spec.grid else ""
     if spec.mode == "topk":
@@ -158,6 +211,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for a profiler")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--unfused", action="store_true",
                     help="with a linear branch: separate sparse, linear and combine calls")
     args = ap.parse_args()
@@ -169,6 +223,7 @@ def main():
     if args.profile:
         args.no_cpu_baseline = True
         args.no_dense = True
+        args.no_backward = True
 
     import torch
     import block_sparse_attention_meanpool_amd as sla
@@ -284,6 +339,11 @@ def main():
         "sparse_kernel_tflops": achieved,
         "pool_classify_gbs_algorithmic": pool_bytes / (stage_ms["pool_classify"] * 1e-3) / 1e9,
     }
+
+    if not args.no_backward and d == 128 and b == 128:
+        extra["backward"] = backward_timing(sla, torch, q, k, v, b, crit_idx, crit_cnt, marg_idx,
+                                            marg_cnt, km, flop, args.steps, stream)
+        log(f"[bench] backward: {extra['backward']}")
 
     if not args.no_dense:
         od = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)

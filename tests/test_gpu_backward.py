@@ -154,3 +154,37 @@ def test_both_branches_backward():
     got, ref = _run_both(spec, cls, ("softmax", "linear"))
     for a, b, n in zip(got, ref, ("dQ", "dK", "dV")):
         _grad_close(a, b, n)
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,heads", [("wan1p3b", (0, 7)), ("wan14b", (13,))])
+def test_backward_workload(name, heads):
+    """Full-size workloads: the GPU computes every head; the oracle checks the
+    listed heads in full (all of their dQ, dK, dV)."""
+    from synth import CONFIGS
+    spec = CONFIGS[name]
+    say(f"[backward workload] {name}: H={spec.H} N={spec.N}, checking heads {heads}")
+    data = generate(spec)
+    g = np.random.default_rng(31)
+    do_bits = _bf16_bits(g.standard_normal((spec.B, spec.H, spec.N, spec.d), dtype=np.float32))
+    q, k, v, d_o = (to_dev(x) for x in (data["q"], data["k"], data["v"], do_bits))
+    b, nb = spec.block, spec.nb
+    sel = "sla3" if spec.mode == "maskin" else spec.mode
+    kc, km = osla.selection_counts(sel, nb, spec.keep, spec.marg)
+    cls = sla.sla_pool_classify(q, k, b, sel, kc, km, spec.thr or 0.0)
+    ci, cc, mi, mc = sla.sla_block_mask(cls, kc, km)
+    o_s, lse = sla.sla_sparse_attn_fwd(q, k, v, b, ci, cc, o_fp32=True, want_lse=True)
+    dq, dk, dv = sla.sla_sparse_attn_bwd(q, k, v, b, ci, cc, o_s, lse, d_o)
+    branches = ("softmax",)
+    if km:
+        lin_ws = sla.sla_linear_branch_prepare(k, v, b, mi, mc)
+        sla.sla_linear_branch_bwd(q, k, v, b, mi, mc, d_o, lin_ws, dq, dk, dv)
+        branches = ("softmax", "linear")
+    torch.cuda.synchronize()
+    cls_np = cls.cpu().numpy()
+    for h in heads:
+        one = lambda x: osla.bf16_to_f64(x[0, h])[None, None]
+        ref = ograd.backward(one(data["q"]), one(data["k"]), one(data["v"]), cls_np[:, h:h + 1], b,
+                             one(do_bits), branches=branches)
+        for t, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
+            _grad_close(t[0, h].cpu().numpy(), r[0, 0], f"{n} head {h}")
