@@ -340,6 +340,14 @@ def main():
         "pool_classify_gbs_algorithmic": pool_bytes / (stage_ms["pool_classify"] * 1e-3) / 1e9,
     }
 
+    # mask quality of this step's critical tiles (outside the timed region)
+    rec = sla.sla_mask_recall(q, k, b, crit_idx, crit_cnt)
+    torch.cuda.synchronize()
+    extra["mask_recall"] = {"mean": float(rec.double().mean().item()),
+                            "min": float(rec.min().item()),
+                            "what": "share of each query's dense softmax mass on its critical tiles"}
+    del rec
+
     if not args.no_backward and d == 128 and b == 128:
         extra["backward"] = backward_timing(sla, torch, q, k, v, b, crit_idx, crit_cnt, marg_idx,
                                             marg_cnt, km, flop, args.steps, stream)

@@ -8,7 +8,7 @@ from .binding import (CLS_CRITICAL, CLS_MARGINAL, CLS_SKIP, EXPORTS, FLAG_BAD_CL
                       LIB_PATH, MODES, SlaError, count_from_fraction, counts_for, forward, lib,
                       num_blocks, sla_block_mask, sla_combine, sla_dense_attn_fwd,
                       sla_linear_branch_bwd, sla_linear_branch_fwd, sla_linear_branch_prepare,
-                      sla_pool_classify,
+                      sla_mask_recall, sla_pool_classify,
                       sla_sparse_attn_bwd, sla_sparse_attn_fwd, sla_sparse_linear_attn_fwd,
                       sla_status_string, sla_version)
 
@@ -16,6 +16,6 @@ __all__ = ["CLS_CRITICAL", "CLS_MARGINAL", "CLS_SKIP", "EXPORTS", "FLAG_BAD_CLAS
            "LIB_PATH", "MODES", "SlaError", "count_from_fraction", "counts_for", "forward", "lib",
            "num_blocks", "sla_block_mask", "sla_combine", "sla_dense_attn_fwd",
            "sla_linear_branch_bwd", "sla_linear_branch_fwd", "sla_linear_branch_prepare",
-           "sla_pool_classify",
+           "sla_mask_recall", "sla_pool_classify",
            "sla_sparse_attn_bwd", "sla_sparse_attn_fwd", "sla_sparse_linear_attn_fwd",
            "sla_status_string", "sla_version"]

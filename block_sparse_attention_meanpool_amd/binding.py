@@ -51,6 +51,9 @@ _SIGS = {
     "sla_linear_branch_bwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _P, _P,
                                      _SZ, _P, _P, _P, _P, _SZ, _P]),
     "sla_linear_branch_bwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32]),
+    "sla_mask_recall": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _F, _P, _P, _SZ,
+                               _P]),
+    "sla_mask_recall_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32]),
     "sla_dense_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _F, _P, _I32, _P, _P]),
     "sla_status_string": (ctypes.c_char_p, [_I32]),
     "sla_version": (_I32, []),
@@ -300,6 +303,27 @@ def sla_linear_branch_bwd(q, k, v, block, marg_idx, marg_cnt, d_o, lin_ws, dq, d
           _ptr(marg_cnt), marg_idx.shape[-1], _ptr(d_o), _ptr(lin_ws), lin_ws.numel(), _ptr(dq),
           _ptr(dk), _ptr(dv), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     return dq, dk, dv
+
+
+def sla_mask_recall(q, k, block, crit_idx, crit_cnt, scale=None, recall=None, ws=None,
+                    stream=None):
+    """Share of each query's dense softmax mass held by its kept tiles, fp32 [B, H, N]."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(k, torch.bfloat16, "k")
+    _dev(crit_idx, torch.int32, "crit_idx")
+    _dev(crit_cnt, torch.int32, "crit_cnt")
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if recall is None:
+        recall = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    need = lib().sla_mask_recall_ws_bytes(B, H, N, d, block)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _call("sla_mask_recall", _ptr(q), _ptr(k), B, H, N, d, block, _ptr(crit_idx), _ptr(crit_cnt),
+          crit_idx.shape[-1], float(scale), _ptr(recall), _ptr(ws), ws.numel() * ws.element_size(),
+          _stream(stream))
+    return recall
 
 
 def sla_combine(o_s, o_lin=None, o=None, stream=None):

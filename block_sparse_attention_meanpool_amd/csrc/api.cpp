@@ -266,6 +266,31 @@ sla_status sla_linear_branch_bwd(const uint16_t* q, const uint16_t* k, const uin
                                          d_o, lin_ws, dq, dk, dv, ws, stream));
 }
 
+size_t sla_mask_recall_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {
+  int64_t nb = 0;
+  if (check_shape(B, H, N, d, block, &nb) != SLA_OK) return 0;
+  return sla::recall_ws_layout(B * H, (int)N, (int)d).total;
+}
+
+sla_status sla_mask_recall(const uint16_t* q, const uint16_t* k, int64_t B, int64_t H, int64_t N,
+                           int64_t d, int32_t block, const int32_t* crit_idx,
+                           const int32_t* crit_cnt, int32_t kc_max, float scale, float* recall,
+                           void* ws, size_t ws_bytes, hipStream_t stream) {
+  int64_t nb = 0;
+  sla_status st = check_shape(B, H, N, d, block, &nb);
+  if (st != SLA_OK) return st;
+  if (!q || !k || !crit_idx || !crit_cnt || !recall) return SLA_ERR_INVALID_ARG;
+  if (kc_max < 1 || kc_max > nb) return SLA_ERR_INVALID_ARG;
+  if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || (reinterpret_cast<uintptr_t>(recall) & 3u))
+    return SLA_ERR_ALIGNMENT;
+  if ((B * H * N + 255) / 256 > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
+  const size_t need = sla_mask_recall_ws_bytes(B, H, N, d, block);
+  if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  return from_hip(sla::launch_recall(q, k, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
+                                     crit_cnt, kc_max, scale, recall, ws, stream));
+}
+
 sla_status sla_combine(const void* o_s, int32_t o_s_is_fp32, const float* o_lin, uint16_t* o,
                        int64_t n_elems, hipStream_t stream) {
   if (!o_s || !o || n_elems < 0 || n_elems % 8 != 0) return SLA_ERR_INVALID_ARG;

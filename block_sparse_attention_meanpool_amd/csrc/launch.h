@@ -85,6 +85,14 @@ hipError_t launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_
                              int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
                              const uint16_t* d_o, const void* lin_ws, float* dq, float* dk,
                              float* dv, void* ws, hipStream_t s);
+// Mask recall workspace: a scratch O (bf16) and the two LSEs (fp32).
+struct RecallWs {
+  size_t o_bytes, lse_bytes, total;
+};
+RecallWs recall_ws_layout(int64_t BH, int N, int d);
+hipError_t launch_recall(const uint16_t* q, const uint16_t* k, int64_t BH, int N, int d, int block,
+                         int nb, const int32_t* idx, const int32_t* cnt, int kmax, float scale,
+                         float* recall, void* ws, hipStream_t s);
 hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,
                           int64_t n_elems, hipStream_t s);
 

@@ -274,6 +274,29 @@ sla_status sla_linear_branch_bwd(const uint16_t* q, const uint16_t* k, const uin
 size_t sla_linear_branch_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block);
 
 /*
+ * Mask quality (Veda article: fidelity to the structure of dense attention,
+ * reported as recall).  For each query token n of query block i:
+ *   recall[n] = sum over the keys m of the tiles in crit_idx[i] of
+ *               softmax over ALL keys of (scale * q_n . k_m),
+ * the share of its dense attention mass that the kept tiles hold, computed as
+ * exp(LSE over the kept keys - LSE over all keys) from one masked and one
+ * dense pass of the attention kernel (bf16 MFMA; each LSE within about 2^-8
+ * of its exact value, so recall is within about 2 * 2^-8 relative; it is not
+ * clamped to 1).  A row with no kept tile gets 0.  A diagnostic: it costs a
+ * dense attention pass.
+ *
+ * recall    fp32 [B, H, N]                                      (out)
+ * ws        device workspace of at least sla_mask_recall_ws_bytes() bytes
+ */
+sla_status sla_mask_recall(const uint16_t* q, const uint16_t* k, int64_t B, int64_t H, int64_t N,
+                           int64_t d, int32_t block, const int32_t* crit_idx,
+                           const int32_t* crit_cnt, int32_t kc_max, float scale, float* recall,
+                           void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes for sla_mask_recall (a scratch O and two LSE arrays). */
+size_t sla_mask_recall_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block);
+
+/*
  * Dense softmax attention with the same kernel core: every key block is kept
  * for every query block.  A baseline for timing the sparse path against.
  */

@@ -302,3 +302,35 @@ def forward(q, k, v, cls, b, scale=None):
         lse[bi, h, lo:hi] = l
         o_lin[bi, h, lo:hi] = c
     return o_s, lse, o_lin, o_s + o_lin
+
+
+# ----------------------------------------------------------------------------
+# mask quality: attention-mass recall (Veda article: fidelity to the structure
+# of dense attention, reported as recall)
+# ----------------------------------------------------------------------------
+
+def mask_recall(q, k, cls, b, scale=None, kept=(CRITICAL,)):
+    """Per query token, the share of its dense softmax attention mass that falls
+    on the keys of the tiles the class map keeps for its query block.
+
+    q, k float64 [B, H, N, d]; cls [B, H, nqb, nkb]; `kept` lists the class
+    codes counted as kept.  Returns float64 [B, H, N] in [0, 1]: the softmax is
+    taken over all N keys (the dense distribution), its entries summed over the
+    kept tokens only.
+    """
+    B, H, N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    nqb = num_blocks(N, b)
+    out = np.zeros((B, H, N))
+    for bi in range(B):
+        for h in range(H):
+            for i in range(nqb):
+                lo, hi = block_bounds(N, b, i)
+                logits = scale * (q[bi, h, lo:hi] @ k[bi, h].T)        # [r, N]
+                blocks = [j for j in range(cls.shape[-1]) if cls[bi, h, i, j] in kept]
+                toks = _tokens_of(blocks, N, b)
+                for r in range(hi - lo):
+                    p = softmax(logits[r])
+                    out[bi, h, lo + r] = p[toks].sum() if len(toks) else 0.0
+    return out
