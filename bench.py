@@ -340,6 +340,25 @@ def main():
         "pool_classify_gbs_algorithmic": pool_bytes / (stage_ms["pool_classify"] * 1e-3) / 1e9,
     }
 
+    # per-head 3D tile order (run on Q, K, V before the path and on O after it)
+    if spec.grid:
+        shape = (2, 8, 8) if b == 128 else (1, 8, 8)
+        if all(g % t == 0 for g, t in zip(spec.grid, shape)):
+            y = torch.empty_like(q)
+            sla.sla_tile_permute(q, spec.grid, [shape] * H, b, y=y)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for t in (q, k, v):
+                sla.sla_tile_permute(t, spec.grid, [shape] * H, b, y=y)
+            sla.sla_tile_permute(o, spec.grid, [shape] * H, b, inverse=True, y=y)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            extra["tile_permute"] = {"tile": shape, "ms_qkv_and_o": ms,
+                                     "gbs": 8 * q.numel() * 2 / (ms * 1e-3) / 1e9}
+            del y
+
     # mask quality of this step's critical tiles (outside the timed region)
     rec = sla.sla_mask_recall(q, k, b, crit_idx, crit_cnt)
     torch.cuda.synchronize()

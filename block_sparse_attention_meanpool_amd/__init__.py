@@ -10,7 +10,7 @@ from .binding import (CLS_CRITICAL, CLS_MARGINAL, CLS_SKIP, EXPORTS, FLAG_BAD_CL
                       sla_linear_branch_bwd, sla_linear_branch_fwd, sla_linear_branch_prepare,
                       sla_mask_recall, sla_pool_classify,
                       sla_sparse_attn_bwd, sla_sparse_attn_fwd, sla_sparse_linear_attn_fwd,
-                      sla_status_string, sla_version)
+                      sla_status_string, sla_tile_permute, sla_version)
 
 __all__ = ["CLS_CRITICAL", "CLS_MARGINAL", "CLS_SKIP", "EXPORTS", "FLAG_BAD_CLASS", "FLAG_OVERFLOW",
            "LIB_PATH", "MODES", "SlaError", "count_from_fraction", "counts_for", "forward", "lib",
@@ -18,4 +18,4 @@ __all__ = ["CLS_CRITICAL", "CLS_MARGINAL", "CLS_SKIP", "EXPORTS", "FLAG_BAD_CLAS
            "sla_linear_branch_bwd", "sla_linear_branch_fwd", "sla_linear_branch_prepare",
            "sla_mask_recall", "sla_pool_classify",
            "sla_sparse_attn_bwd", "sla_sparse_attn_fwd", "sla_sparse_linear_attn_fwd",
-           "sla_status_string", "sla_version"]
+           "sla_status_string", "sla_tile_permute", "sla_version"]

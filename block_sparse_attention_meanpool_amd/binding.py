@@ -54,6 +54,7 @@ _SIGS = {
     "sla_mask_recall": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _F, _P, _P, _SZ,
                                _P]),
     "sla_mask_recall_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32]),
+    "sla_tile_permute": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I32, _P]),
     "sla_dense_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _F, _P, _I32, _P, _P]),
     "sla_status_string": (ctypes.c_char_p, [_I32]),
     "sla_version": (_I32, []),
@@ -326,6 +327,23 @@ def sla_mask_recall(q, k, block, crit_idx, crit_cnt, scale=None, recall=None, ws
     return recall
 
 
+def sla_tile_permute(x, grid, tiles, block, inverse=False, y=None, stream=None):
+    """Rows of x [B, H, T*Y*X, d] into per-head 3D tile order (or back, inverse=True).
+
+    grid = (T, Y, X); tiles = one (bt, by, bx) per head (host ints)."""
+    _dev(x, torch.bfloat16, "x")
+    B, H, N, d = x.shape
+    T, Y, X = (int(g) for g in grid)
+    if len(tiles) != H:
+        raise ValueError(f"need one tile shape per head ({H}), got {len(tiles)}")
+    arr = (ctypes.c_int32 * (3 * H))(*[int(t) for shape in tiles for t in shape])
+    if y is None:
+        y = torch.empty_like(x)
+    _call("sla_tile_permute", _ptr(x), _ptr(y), B, H, T, Y, X, d, int(block),
+          ctypes.cast(arr, ctypes.c_void_p), int(bool(inverse)), _stream(stream))
+    return y
+
+
 def sla_combine(o_s, o_lin=None, o=None, stream=None):
     if o is None:
         o = torch.empty(o_s.shape, dtype=torch.bfloat16, device=o_s.device)
@@ -351,14 +369,16 @@ def forward(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=Non
     """
     B, H, N, d = q.shape
     nb = num_blocks(N, block)
-    kc, km = counts_for(mode, nb, keep, marg)
     if cls is None:
+        kc, km = counts_for(mode, nb, keep, marg)
         cls = sla_pool_classify(q, k, block, mode, kc, km, thr or 0.0, stream=stream)
         kc_max = nb if mode == "cdf" else kc
         km_max = km
     else:
-        kc_max = kc if keep is not None else nb
-        km_max = km if marg is not None else nb
+        # a given map: the fractions, when given, only size the lists
+        kc_max = count_from_fraction(keep, nb) if keep is not None else nb
+        km_max = (counts_for("sla3", nb, keep, marg)[1] if keep is not None and marg is not None
+                  else nb)
     crit_idx, crit_cnt, marg_idx, marg_cnt = sla_block_mask(cls, kc_max, km_max, stream=stream)
     out = {"cls": cls, "crit_idx": crit_idx, "crit_cnt": crit_cnt, "marg_idx": marg_idx,
            "marg_cnt": marg_cnt}

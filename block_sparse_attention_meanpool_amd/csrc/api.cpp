@@ -291,6 +291,35 @@ sla_status sla_mask_recall(const uint16_t* q, const uint16_t* k, int64_t B, int6
                                      crit_cnt, kc_max, scale, recall, ws, stream));
 }
 
+sla_status sla_tile_permute(const uint16_t* x, uint16_t* y, int64_t B, int64_t H, int64_t T,
+                            int64_t Y, int64_t X, int64_t d, int32_t block, const int32_t* tiles,
+                            int32_t inverse, hipStream_t stream) {
+  if (!x || !y || !tiles || x == y) return SLA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || T < 1 || Y < 1 || X < 1) return SLA_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return SLA_ERR_UNSUPPORTED;
+  if (H > sla::kMaxTileHeads) return SLA_ERR_UNSUPPORTED;
+  if (T > INT32_MAX / Y || T * Y > INT32_MAX / X) return SLA_ERR_UNSUPPORTED;
+  const int64_t N = T * Y * X;
+  int64_t nb = 0;
+  sla_status st = check_shape(B, H, N, d, block, &nb);
+  if (st != SLA_OK) return st;
+  if (!aligned16(x) || !aligned16(y)) return SLA_ERR_ALIGNMENT;
+  if (N * (d / 8) > INT32_MAX) return SLA_ERR_UNSUPPORTED;
+  sla::TileShapes ts{};
+  for (int64_t h = 0; h < H; ++h) {
+    const int32_t bt = tiles[3 * h], by = tiles[3 * h + 1], bx = tiles[3 * h + 2];
+    if (bt < 1 || by < 1 || bx < 1) return SLA_ERR_INVALID_ARG;
+    if (T % bt || Y % by || X % bx) return SLA_ERR_INVALID_ARG;
+    if ((int64_t)bt * by * bx != block) return SLA_ERR_INVALID_ARG;
+    // block is 64 or 128, so each side is a power of two: store log2
+    ts.s[h][0] = (int16_t)__builtin_ctz((unsigned)bt);
+    ts.s[h][1] = (int16_t)__builtin_ctz((unsigned)by);
+    ts.s[h][2] = (int16_t)__builtin_ctz((unsigned)bx);
+  }
+  return from_hip(sla::launch_tile_permute(x, y, B * H, (int)H, (int)T, (int)Y, (int)X, (int)d, ts,
+                                           inverse != 0, stream));
+}
+
 sla_status sla_combine(const void* o_s, int32_t o_s_is_fp32, const float* o_lin, uint16_t* o,
                        int64_t n_elems, hipStream_t stream) {
   if (!o_s || !o || n_elems < 0 || n_elems % 8 != 0) return SLA_ERR_INVALID_ARG;

@@ -93,6 +93,14 @@ RecallWs recall_ws_layout(int64_t BH, int N, int d);
 hipError_t launch_recall(const uint16_t* q, const uint16_t* k, int64_t BH, int N, int d, int block,
                          int nb, const int32_t* idx, const int32_t* cnt, int kmax, float scale,
                          float* recall, void* ws, hipStream_t s);
+// Per-head tile shapes as log2 of (bt, by, bx), passed by value in the kernel
+// arguments.
+constexpr int kMaxTileHeads = 256;
+struct TileShapes {
+  int16_t s[kMaxTileHeads][3];
+};
+hipError_t launch_tile_permute(const uint16_t* x, uint16_t* y, int64_t BH, int H, int T, int Y,
+                               int X, int d, const TileShapes& ts, int inverse, hipStream_t s);
 hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,
                           int64_t n_elems, hipStream_t s);
 

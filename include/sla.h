@@ -297,6 +297,26 @@ sla_status sla_mask_recall(const uint16_t* q, const uint16_t* k, int64_t B, int6
 size_t sla_mask_recall_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block);
 
 /*
+ * Per-head 3D token tiles (Veda article, context: heads get their own tile
+ * shapes).  x holds the tokens of a (T, Y, X) latent grid in raster order
+ * n = (t Y + y) X + x.  Head h's tile shape (bt, by, bx) = tiles[3h .. 3h+2]
+ * cuts the grid into boxes; the tile order lists the boxes in raster order of
+ * their box index and, inside a box, its tokens in raster order, so that each
+ * block of `block` = bt*by*bx consecutive tokens is one box.  With
+ * inverse = 0, y = x rearranged into tile order (run on Q, K, V before the
+ * path); with inverse != 0, y = x rearranged from tile order back to raster
+ * order (run on O).  Rows are copied bit for bit.
+ *
+ * x, y      bf16 [B, H, T*Y*X, d], distinct buffers        (in / out)
+ * tiles     HOST int32 [H][3]; each shape must divide (T, Y, X) and have
+ *           volume `block` (otherwise SLA_ERR_INVALID_ARG)
+ * Supported: d in {64, 128}, H <= 256.
+ */
+sla_status sla_tile_permute(const uint16_t* x, uint16_t* y, int64_t B, int64_t H, int64_t T,
+                            int64_t Y, int64_t X, int64_t d, int32_t block, const int32_t* tiles,
+                            int32_t inverse, hipStream_t stream);
+
+/*
  * Dense softmax attention with the same kernel core: every key block is kept
  * for every query block.  A baseline for timing the sparse path against.
  */

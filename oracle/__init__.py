@@ -19,6 +19,8 @@ What it computes, and where the pages say so:
 
 * SLA post ("results"): the method is trainable with a short fine-tuning;
   ``grad.py`` holds the gradients of the forward with the class map fixed.
+* Veda article ("context"): heads get their own tile shapes; ``tiles.py``
+  orders the tokens of a latent grid into per-head 3D boxes.
 
 Every function is the plain definition, in fp64, with numpy BLAS matmuls as
 the only library step.  Readings of points the pages leave open are listed in
@@ -32,4 +34,4 @@ on the structured workloads have no published number to hit; they are pinned
 only through those parts.
 """
 
-from . import grad, sla  # noqa: F401
+from . import grad, sla, tiles  # noqa: F401

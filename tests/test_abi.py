@@ -146,6 +146,25 @@ def test_other_entry_points_reject_bad_arguments(mod):
     assert lib.sla_combine(None, 1, None, GOOD, 16, None) == -1
 
 
+def test_tile_permute_rejects_bad_arguments(mod):
+    lib = mod.lib()
+    tp = lib.sla_tile_permute
+
+    def tiles(*shapes):
+        flat = [t for shape in shapes for t in shape]
+        return ctypes.cast((ctypes.c_int32 * len(flat))(*flat), ctypes.c_void_p)
+
+    ok = tiles((1, 8, 8), (2, 4, 8))
+    # grid 4 x 8 x 16, two heads, block 64
+    assert tp(GOOD, GOOD, 1, 2, 4, 8, 16, 128, 64, ok, 0, None) == -1        # in place
+    assert tp(GOOD, P(0x20000), 1, 2, 4, 8, 16, 128, 64, tiles((3, 8, 8), (2, 4, 8)), 0,
+              None) == -1                                                   # 3 does not divide 4
+    assert tp(GOOD, P(0x20000), 1, 2, 4, 8, 16, 128, 128, ok, 0, None) == -1  # volume != block
+    assert tp(GOOD, P(0x20000), 1, 2, 4, 8, 16, 96, 64, ok, 0, None) == -2
+    assert tp(ODD, P(0x20000), 1, 2, 4, 8, 16, 128, 64, ok, 0, None) == -3
+    assert tp(GOOD, P(0x20000), 1, 2, 4, 8, 16, 128, 64, None, 0, None) == -1
+
+
 def test_binding_refuses_cpu_tensors(mod):
     torch = pytest.importorskip("torch")
     q = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
