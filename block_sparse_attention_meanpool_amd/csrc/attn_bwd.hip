@@ -125,6 +125,10 @@ __device__ __forceinline__ void dq_half(const char* kbuf, const char* vbuf, cons
       dpacc[kb] = mfma32x32x16(dual_row_read(vbuf, 32 * kb + krow, 2 * ks + hf), dof[ks], dpacc[kb]);
     }
   }
+  // Scheduling hints (LLVM's interleave strategies) for the MFMA chains with
+  // their LDS reads and for the exp2 softmax with the dQ MFMAs; instruction
+  // order only, results bit-identical.
+  __builtin_amdgcn_iglp_opt(1);
   if (key0 + HALF > N) {
     // register r of block kb holds key key0 + 8 hf + (32 kb + r + 8 [r >= 8])
     const int lim = N - key0 - 8 * hf;
@@ -151,6 +155,7 @@ __device__ __forceinline__ void dq_half(const char* kbuf, const char* vbuf, cons
 #pragma unroll
     for (int db = 0; db < 4; ++db)
       dqacc[db] = mfma32x32x16(tr_operand<DualSwz>(kbuf, 16 * ks2, 32 * db, lane), dsb[ks2], dqacc[db]);
+  __builtin_amdgcn_iglp_opt(2);
 }
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dq_kernel(
@@ -313,6 +318,7 @@ __device__ __forceinline__ void dkdv_half(const char* qbuf, const char* obuf, co
         dkacc[db] = mfma32x32x16(tr_operand<DualSwz>(qbuf, k0, 32 * db, lane), dsb, dkacc[db]);
       }
     }
+    __builtin_amdgcn_iglp_opt(2);  // interleave the exp2 work with the MFMAs (order only)
   }
 }
 

@@ -267,6 +267,10 @@ __device__ __forceinline__ void compute_half(const char* kbuf, const char* vbuf,
       sacc[kb] = mfma32x32x16(a, qf[ks], sacc[kb]);
     }
   }
+  // Scheduling hints (LLVM's interleave strategies): the S^T MFMAs with their
+  // LDS operand reads, and below the exp2 softmax with the P V MFMAs.  They
+  // reorder instructions only; results are bit-identical, ~2% faster here.
+  __builtin_amdgcn_iglp_opt(1);
   if (key0 + HALF > N) {
     // register r of block kb holds key key0 + 8 hf + (32 kb + r + 8 [r >= 8])
     const int lim = N - key0 - 8 * hf;
@@ -312,6 +316,7 @@ __device__ __forceinline__ void compute_half(const char* kbuf, const char* vbuf,
     for (int db = 0; db < 4; ++db)
       oacc[db] = mfma32x32x16(tr_operand(vbuf, 16 * ks2, 32 * db, lane), pb[ks2], oacc[db]);
   }
+  __builtin_amdgcn_iglp_opt(2);
   (void)l32;
 }
 
