@@ -341,7 +341,7 @@ def main():
     }
 
     # per-head 3D tile order (run on Q, K, V before the path and on O after it)
-    if spec.grid:
+    if spec.grid and not args.profile:
         shape = (2, 8, 8) if b == 128 else (1, 8, 8)
         if all(g % t == 0 for g, t in zip(spec.grid, shape)):
             y = torch.empty_like(q)
@@ -360,12 +360,13 @@ def main():
             del y
 
     # mask quality of this step's critical tiles (outside the timed region)
-    rec = sla.sla_mask_recall(q, k, b, crit_idx, crit_cnt)
-    torch.cuda.synchronize()
-    extra["mask_recall"] = {"mean": float(rec.double().mean().item()),
-                            "min": float(rec.min().item()),
-                            "what": "share of each query's dense softmax mass on its critical tiles"}
-    del rec
+    if not args.profile:
+        rec = sla.sla_mask_recall(q, k, b, crit_idx, crit_cnt)
+        torch.cuda.synchronize()
+        extra["mask_recall"] = {"mean": float(rec.double().mean().item()),
+                                "min": float(rec.min().item()),
+                                "what": "share of each query's dense softmax mass on its critical tiles"}
+        del rec
 
     if not args.no_backward and d == 128 and b == 128:
         extra["backward"] = backward_timing(sla, torch, q, k, v, b, crit_idx, crit_cnt, marg_idx,
