@@ -340,6 +340,6 @@ const char* sla_status_string(sla_status status) {
   }
 }
 
-int32_t sla_version(void) { return 200; }
+int32_t sla_version(void) { return 300; }
 
 }  // extern "C"

@@ -30,13 +30,24 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   const int c = t % CH, r0 = t / CH;
   const int row0 = blk * block;
   const int valid = min(block, N - row0);
+  // All of this thread's rows (at most 128 / RS) are loaded before the first
+  // add, so their latencies overlap; rows past the block's end read as 0 and
+  // the sums run in row order as before.
+  constexpr int MAXS = 128 / RS;
+  u32x4 xs[MAXS];
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    const int r = r0 + s * RS;
+    xs[s] = r < valid ? buf_load16(rs, (uint32_t)((row0 + r) * D + c * 8) * 2) : u32x4{};
+  }
   float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r = r0; r < valid; r += RS) {
-    u32x4 x = buf_load16(rs, (uint32_t)((row0 + r) * D + c * 8) * 2);
+#pragma unroll
+  for (int s = 0; s < MAXS; ++s) {
+    if (r0 + s * RS >= valid) break;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      acc[2 * e] += bf16_bits_to_f32(x[e] & 0xffffu);
-      acc[2 * e + 1] += bf16_bits_to_f32(x[e] >> 16);
+      acc[2 * e] += bf16_bits_to_f32(xs[s][e] & 0xffffu);
+      acc[2 * e + 1] += bf16_bits_to_f32(xs[s][e] >> 16);
     }
   }
 #pragma unroll

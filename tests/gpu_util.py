@@ -2,7 +2,7 @@
 small workloads with margin repairs from the oracle, and the comparison bars.
 
 Bars (the ones stated for this path): block masks and lists bit-exact;
-outputs within max-abs 2e-2 and relative L2 5e-3 of the fp64 oracle, judged
+outputs within max-abs 2e-2 and relative L2 5e-3 of the fp64 oracle, evaluated
 on the kernels' fp32 outputs before the final bf16 rounding; the bf16 output
 must equal the round-to-nearest-even of that fp32 output.
 """
