@@ -203,7 +203,7 @@ sla_status sla_sparse_linear_attn_fwd(const uint16_t* q, const uint16_t* k, cons
 
 size_t sla_sparse_attn_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {
   int64_t nb = 0;
-  if (check_shape(B, H, N, d, block, &nb) != SLA_OK || d != 128 || block != 128) return 0;
+  if (check_shape(B, H, N, d, block, &nb) != SLA_OK) return 0;
   return sla::attn_bwd_ws_layout(B * H, (int)N, (int)nb).total;
 }
 
@@ -216,7 +216,6 @@ sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
   int64_t nb = 0;
   sla_status st = check_shape(B, H, N, d, block, &nb);
   if (st != SLA_OK) return st;
-  if (d != 128 || block != 128) return SLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !crit_idx || !crit_cnt || !o_s || !lse || !d_o || !dq || !dk || !dv)
     return SLA_ERR_INVALID_ARG;
   if (kc_max < 1 || kc_max > nb) return SLA_ERR_INVALID_ARG;
@@ -228,9 +227,9 @@ sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
   if ((BH * nb * kc_max + 255) / 256 > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
   const size_t need = sla_sparse_attn_bwd_ws_bytes(B, H, N, d, block);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
-  return from_hip(sla::launch_attn_bwd(q, k, v, BH, (int)N, (int)nb, crit_idx, crit_cnt, kc_max,
-                                       scale, o_s, o_s_is_fp32 != 0, lse, d_o, dq, dk, dv, ws,
-                                       stream));
+  return from_hip(sla::launch_attn_bwd(q, k, v, BH, (int)N, (int)d, block, (int)nb, crit_idx,
+                                       crit_cnt, kc_max, scale, o_s, o_s_is_fp32 != 0, lse, d_o,
+                                       dq, dk, dv, ws, stream));
 }
 
 size_t sla_linear_branch_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {

@@ -424,7 +424,8 @@ AttnBwdWs attn_bwd_ws_layout(int64_t BH, int N, int nb) {
 }
 
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
-                           int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
+                           int N, int d, int block, int nb, const int32_t* idx, const int32_t* cnt,
+                           int kmax,
                            float scale, const void* o_s, int o_fp32, const float* lse,
                            const uint16_t* d_o, float* dq, float* dk, float* dv, void* ws,
                            hipStream_t s) {
@@ -442,6 +443,9 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                                                                           col_idx, col_cnt);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (d != bwd::D || block != bwd::BLK)
+    return launch_attn_bwd_generic(q, k, v, BH, N, d, block, nb, idx, cnt, kmax, scale, o_s, o_fp32,
+                                   lse, d_o, dq, dk, dv, Dbuf, col_idx, col_cnt, s);
   const int seg = (nb + 7) / 8;
   const dim3 grid((unsigned)(BH * seg * 8));
   const float sl2 = scale * kLog2e;

@@ -66,12 +66,21 @@ struct AttnBwdWs {
   size_t d_bytes, bits_bytes, cnt_bytes, idx_bytes, total;
 };
 AttnBwdWs attn_bwd_ws_layout(int64_t BH, int N, int nb);
-// d = 128, block = 128 only; dq, dk, dv fp32, overwritten
+// d in {64, 128}, block in {64, 128}; dq, dk, dv fp32, overwritten
 hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
-                           int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
-                           float scale, const void* o_s, int o_fp32, const float* lse,
+                           int N, int d, int block, int nb, const int32_t* idx, const int32_t* cnt,
+                           int kmax, float scale, const void* o_s, int o_fp32, const float* lse,
                            const uint16_t* d_o, float* dq, float* dk, float* dv, void* ws,
                            hipStream_t s);
+// the two gradient kernels for the shapes other than d = 128 with 128-token
+// blocks, given D and the column lists built by launch_attn_bwd
+hipError_t launch_attn_bwd_generic(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                   int64_t BH, int N, int d, int block, int nb,
+                                   const int32_t* idx, const int32_t* cnt, int kmax, float scale,
+                                   const void* o_s, int o_fp32, const float* lse,
+                                   const uint16_t* d_o, float* dq, float* dk, float* dv,
+                                   float* Dbuf, const uint16_t* col_idx, const int32_t* col_cnt,
+                                   hipStream_t s);
 // Linear-branch backward workspace: dS_i (bf16, laid out like the states),
 // dzeta_i (fp32), the transposed marginal bit matrix, dH_j (bf16), dz_j (fp32).
 struct LinearBwdWs {

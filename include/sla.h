@@ -227,7 +227,8 @@ sla_status sla_combine(const void* o_s, int32_t o_s_is_fp32, const float* o_lin,
  * d_o       bf16 [B, H, N, d]                                   (in)
  * dq, dk, dv  fp32 [B, H, N, d], overwritten                    (out)
  * ws        device workspace of at least sla_sparse_attn_bwd_ws_bytes() bytes
- * Supported: d = 128, block = 128 (SLA_ERR_UNSUPPORTED otherwise).
+ * Every shape the forward takes (d = 64 or 128, blocks of 64 or 128 tokens);
+ * d = 128 with 128-token blocks runs the pipelined kernels.
  */
 sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                                int64_t H, int64_t N, int64_t d, int32_t block,

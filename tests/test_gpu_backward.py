@@ -85,6 +85,31 @@ def test_softmax_backward_small(o_fp32):
     assert not got[0][0, 0, 128:256].any()
 
 
+@pytest.mark.parametrize("d,block,N", [(64, 64, 1000), (64, 128, 1000), (128, 64, 1000),
+                                       (64, 64, 64), (128, 64, 200)])
+def test_softmax_backward_other_shapes(d, block, N):
+    """The generic kernels (every shape but d = 128 with 128-token blocks)."""
+    nb = -(-N // block)
+    spec = Spec(304, f"bwd_d{d}_b{block}", B=1, H=2, N=N, d=d, block=block, kind="fourier",
+                grid=(1, 1, N) if N < 100 else (10, 10, N // 100), mode="topk", keep=F(1, 2))
+    say(f"[backward] softmax branch, d={d}, block={block}, N={N} (nb={nb})")
+    if nb >= 5:
+        cls = _mask(nb, spec.H, 12)
+    else:
+        g = np.random.default_rng(13)
+        cls = np.where(g.random((1, spec.H, nb, nb)) < 0.6, osla.CRITICAL, osla.SKIP).astype(np.uint8)
+        cls[0, 0, 0] = osla.CRITICAL
+    for o_fp32 in (True, False):
+        got, ref = _run(spec, cls, o_fp32)
+        rel = REL_L2 if o_fp32 else 2 * REL_L2
+        for a, b, n in zip(got, ref, ("dQ", "dK", "dV")):
+            _grad_close(a, b, f"{n} o_s fp32={o_fp32}", rel_l2=rel)
+    if nb >= 5:
+        # the key tile no query block uses and the row with no tile get exactly nothing
+        assert not got[1][0, 1, 3 * block:4 * block].any() and not got[2][0, 1, 3 * block:4 * block].any()
+        assert not got[0][0, 0, block:2 * block].any()
+
+
 def test_softmax_backward_selected_mask():
     spec = Spec(302, "bwd_topk", B=1, H=3, N=4000, d=128, block=128, kind="fourier",
                 grid=(10, 20, 20), mode="topk", keep=F(1, 4))
@@ -157,7 +182,8 @@ def test_both_branches_backward():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,heads", [("wan1p3b", (0, 7)), ("wan14b", (13,))])
+@pytest.mark.parametrize("name,heads", [("tiny", (0, 1)), ("short_video", (0, 11)),
+                                        ("wan1p3b", (0, 7)), ("wan14b", (13,))])
 def test_backward_workload(name, heads):
     """Full-size workloads: the GPU computes every head; the oracle checks the
     listed heads in full (all of their dQ, dK, dV)."""
@@ -172,7 +198,7 @@ def test_backward_workload(name, heads):
     sel = "sla3" if spec.mode == "maskin" else spec.mode
     kc, km = osla.selection_counts(sel, nb, spec.keep, spec.marg)
     cls = sla.sla_pool_classify(q, k, b, sel, kc, km, spec.thr or 0.0)
-    ci, cc, mi, mc = sla.sla_block_mask(cls, kc, km)
+    ci, cc, mi, mc = sla.sla_block_mask(cls, nb if sel == "cdf" else kc, km)
     o_s, lse = sla.sla_sparse_attn_fwd(q, k, v, b, ci, cc, o_fp32=True, want_lse=True)
     dq, dk, dv = sla.sla_sparse_attn_bwd(q, k, v, b, ci, cc, o_s, lse, d_o)
     branches = ("softmax",)
