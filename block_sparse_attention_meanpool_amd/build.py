@@ -21,7 +21,8 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "pool_classify.hip", "block_mask.hip", "sparse_attn.hip", "linear_branch.hip",
-           "attn_bwd.hip", "attn_bwd_generic.hip", "linear_bwd.hip", "recall.hip",
+           "attn_bwd.hip", "attn_bwd_generic.hip", "linear_bwd.hip",
+           "linear_bwd_generic.hip", "recall.hip",
            "tile_permute.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -234,8 +234,8 @@ sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
 
 size_t sla_linear_branch_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {
   int64_t nb = 0;
-  if (check_shape(B, H, N, d, block, &nb) != SLA_OK || d != 128 || block != 128) return 0;
-  return sla::linear_bwd_ws_layout(B * H, (int)nb).total;
+  if (check_shape(B, H, N, d, block, &nb) != SLA_OK) return 0;
+  return sla::linear_bwd_ws_layout(B * H, (int)nb, (int)d).total;
 }
 
 sla_status sla_linear_branch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
@@ -247,7 +247,6 @@ sla_status sla_linear_branch_bwd(const uint16_t* q, const uint16_t* k, const uin
   int64_t nb = 0;
   sla_status st = check_shape(B, H, N, d, block, &nb);
   if (st != SLA_OK) return st;
-  if (d != 128 || block != 128) return SLA_ERR_UNSUPPORTED;
   if (!q || !k || !v || !marg_idx || !marg_cnt || !d_o || !dq || !dk || !dv)
     return SLA_ERR_INVALID_ARG;
   if (km_max < 1 || km_max > nb) return SLA_ERR_INVALID_ARG;
@@ -261,8 +260,8 @@ sla_status sla_linear_branch_bwd(const uint16_t* q, const uint16_t* k, const uin
     return SLA_ERR_WORKSPACE;
   const size_t need = sla_linear_branch_bwd_ws_bytes(B, H, N, d, block);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
-  return from_hip(sla::launch_linear_bwd(q, k, v, BH, (int)N, (int)nb, marg_idx, marg_cnt, km_max,
-                                         d_o, lin_ws, dq, dk, dv, ws, stream));
+  return from_hip(sla::launch_linear_bwd(q, k, v, BH, (int)N, (int)d, block, (int)nb, marg_idx,
+                                         marg_cnt, km_max, d_o, lin_ws, dq, dk, dv, ws, stream));
 }
 
 size_t sla_mask_recall_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {

@@ -30,29 +30,7 @@ namespace gbwd {
 template <int D, int BLK>
 __device__ __forceinline__ void stage(const __amdgpu_buffer_rsrc_t& r, int row0, char* rows,
                                       char* tr, int tid) {
-  constexpr int NT = BLK * 2, CH = D / 8, NSUB = (BLK / 8) * (D / 8);
-#pragma unroll
-  for (int s0 = 0; s0 < NSUB; s0 += NT) {
-    const int s = s0 + tid;
-    if (NSUB % NT == 0 || s < NSUB) {
-      int tc, fc;
-      subblock_coords<BLK, D>(s, tc, fc);
-      u32x4 in[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        in[e] = buf_load16(r, (uint32_t)((row0 + 8 * tc + e) * D + 8 * fc) * 2);
-      if (rows) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) *(u32x4*)(rows + row_offset<CH>(8 * tc + e, fc)) = in[e];
-      }
-      if (tr) {
-        u32x4 out[8];
-        transpose8x8(in, out);
-#pragma unroll
-        for (int f = 0; f < 8; ++f) *(u32x4*)(tr + tr_offset<BLK>(8 * fc + f, tc)) = out[f];
-      }
-    }
-  }
+  stage_subblocks<BLK, D, BLK * 2>(r, row0, rows, tr, tid, KeepChunk{});
 }
 
 template <int D, int BLK>

@@ -87,13 +87,22 @@ struct LinearBwdWs {
   int words;
   size_t ds_bytes, dzeta_bytes, bits_bytes, dh_bytes, dz_bytes, total;
 };
-LinearBwdWs linear_bwd_ws_layout(int64_t BH, int nb);
-// d = 128, block = 128 only; lin_ws prepared by launch_linear_prepare for the
-// same inputs; dq, dk, dv fp32, accumulated into
+LinearBwdWs linear_bwd_ws_layout(int64_t BH, int nb, int d);
+// d in {64, 128}, block in {64, 128}; lin_ws prepared by launch_linear_prepare
+// for the same inputs; dq, dk, dv fp32, accumulated into
 hipError_t launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
-                             int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
-                             const uint16_t* d_o, const void* lin_ws, float* dq, float* dk,
-                             float* dv, void* ws, hipStream_t s);
+                             int N, int d, int block, int nb, const int32_t* idx, const int32_t* cnt,
+                             int kmax, const uint16_t* d_o, const void* lin_ws, float* dq,
+                             float* dk, float* dv, void* ws, hipStream_t s);
+// the query-side and key-side kernels of the linear-branch backward for the
+// shapes other than d = 128 with 128-token blocks
+hipError_t launch_linear_bwd_query_generic(const uint16_t* q, const uint16_t* d_o, int64_t BH,
+                                           int N, int d, int block, int nb, const uint16_t* C,
+                                           const float* zeta, float* dq, uint16_t* dS,
+                                           float* dzeta, hipStream_t s);
+hipError_t launch_linear_bwd_key_generic(const uint16_t* k, const uint16_t* v, int64_t BH, int N,
+                                         int d, int block, int nb, const uint16_t* dH,
+                                         const float* dz, float* dk, float* dv, hipStream_t s);
 // Mask recall workspace: a scratch O (bf16) and the two LSEs (fp32).
 struct RecallWs {
   size_t o_bytes, lse_bytes, total;

@@ -9,7 +9,9 @@
 //                                                   (the transposed mask GEMM)
 //   dk_m  += (dH_j v_m + dz_j) * phi'(k_m),  dv_m += dH_j^T phi(k_m)
 //                                                   (key side, per tile)
-// d = 128, 128-token blocks; dq, dk, dv are fp32 and accumulated into.
+// These kernels serve d = 128 with 128-token blocks (the other shapes run the
+// query and key kernels of linear_bwd_generic.hip around the same gather);
+// dq, dk, dv are fp32 and accumulated into.
 #include "common.h"
 #include "launch.h"
 #include "linear_apply.h"
@@ -242,9 +244,8 @@ __global__ __launch_bounds__(NT) void lin_bwd_key_kernel(const uint16_t* __restr
 
 }  // namespace lbwd
 
-LinearBwdWs linear_bwd_ws_layout(int64_t BH, int nb) {
+LinearBwdWs linear_bwd_ws_layout(int64_t BH, int nb, int D) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
-  constexpr int D = lbwd::D;
   LinearBwdWs w;
   w.words = 2 * ((nb + 63) / 64);
   w.ds_bytes = up((size_t)BH * nb * D * D * 2);
@@ -257,12 +258,12 @@ LinearBwdWs linear_bwd_ws_layout(int64_t BH, int nb) {
 }
 
 hipError_t launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
-                             int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
-                             const uint16_t* d_o, const void* lin_ws, float* dq, float* dk,
-                             float* dv, void* ws, hipStream_t s) {
-  constexpr int D = lbwd::D;
+                             int N, int D, int block, int nb, const int32_t* idx, const int32_t* cnt,
+                             int kmax, const uint16_t* d_o, const void* lin_ws, float* dq,
+                             float* dk, float* dv, void* ws, hipStream_t s) {
+  const bool tuned = D == lbwd::D && block == lbwd::BLK;
   const LinearPtrs lp = linear_ws_ptrs(const_cast<void*>(lin_ws), BH, nb, D);
-  const LinearBwdWs lw = linear_bwd_ws_layout(BH, nb);
+  const LinearBwdWs lw = linear_bwd_ws_layout(BH, nb, D);
   char* p = static_cast<char*>(ws);
   uint16_t* dS = reinterpret_cast<uint16_t*>(p);
   p += lw.ds_bytes;
@@ -275,8 +276,13 @@ hipError_t launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_
   float* dz = reinterpret_cast<float*>(p);
 
   const dim3 grid((unsigned)(BH * nb));
-  lbwd::lin_bwd_query_kernel<<<grid, lbwd::NT, 0, s>>>(q, d_o, N, nb, lp.C, lp.zeta, dq, dS, dzeta);
-  hipError_t e = hipGetLastError();
+  hipError_t e;
+  if (tuned) {
+    lbwd::lin_bwd_query_kernel<<<grid, lbwd::NT, 0, s>>>(q, d_o, N, nb, lp.C, lp.zeta, dq, dS, dzeta);
+    e = hipGetLastError();
+  } else {
+    e = launch_linear_bwd_query_generic(q, d_o, BH, N, D, block, nb, lp.C, lp.zeta, dq, dS, dzeta, s);
+  }
   if (e != hipSuccess) return e;
   e = launch_col_bits(idx, cnt, kmax, BH, nb, nb, lw.words, bitsT, s);
   if (e != hipSuccess) return e;
@@ -284,6 +290,7 @@ hipError_t launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_
   if (e != hipSuccess) return e;
   e = launch_bitrow_sums(bitsT, lw.words, BH * nb, nb, nb, dzeta, dz, D, s);
   if (e != hipSuccess) return e;
+  if (!tuned) return launch_linear_bwd_key_generic(k, v, BH, N, D, block, nb, dH, dz, dk, dv, s);
   lbwd::lin_bwd_key_kernel<<<grid, lbwd::NT, 0, s>>>(k, v, N, nb, dH, dz, dk, dv);
   return hipGetLastError();
 }

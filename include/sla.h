@@ -262,7 +262,7 @@ size_t sla_sparse_attn_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, 
  * dq, dk, dv  fp32 [B, H, N, d]: the gradients are ADDED to their contents,
  *           so a call after sla_sparse_attn_bwd yields both branches' sum
  * ws        device workspace of at least sla_linear_branch_bwd_ws_bytes() bytes
- * Supported: d = 128, block = 128 (SLA_ERR_UNSUPPORTED otherwise).
+ * Every shape the forward takes (d = 64 or 128, blocks of 64 or 128 tokens).
  */
 sla_status sla_linear_branch_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                                  int64_t H, int64_t N, int64_t d, int32_t block,

@@ -91,6 +91,39 @@ def linear_block_grad(q_rows, k, v, marg_blocks, b, d_o):
     return dq, toks, dk, dv
 
 
+def linear_dq_scale(q, k, v, cls, b, d_o):
+    """Size of the terms of the linear branch's dQ (float64 [B, H, N, d]):
+    (|dU| |S|^T + |dw| |zeta|^T) * |phi'(Q)| per query block, with the symbols
+    of the header.
+
+    dQ is the difference of dU S^T and dw zeta^T, which nearly cancel: when
+    every value row is the same vector, O_lin equals it and dQ is exactly 0.
+    A computation that rounds S or dU to a finite precision therefore errs in
+    proportion to the size of these terms, not of their difference; this is
+    that size, the scale a tolerance on dQ is measured against.
+    """
+    B, H, N, d = q.shape
+    out = np.zeros_like(q)
+    for bi in range(B):
+        for h in range(H):
+            for i in range(sla.num_blocks(N, b)):
+                lo, hi = sla.block_bounds(N, b, i)
+                toks = sla._tokens_of(np.nonzero(cls[bi, h, i] == sla.MARGINAL)[0], N, b)
+                if len(toks) == 0:
+                    continue
+                a = sla.phi(q[bi, h, lo:hi])
+                ph = sla.phi(k[bi, h, toks])
+                state = ph.T @ v[bi, h, toks]
+                zeta = ph.sum(axis=0)
+                w = a @ zeta
+                o_lin = (a @ state) / w[:, None]
+                du = d_o[bi, h, lo:hi] / w[:, None]
+                dw = -(d_o[bi, h, lo:hi] * o_lin).sum(axis=1) / w
+                mag = np.abs(du) @ np.abs(state).T + np.outer(np.abs(dw), np.abs(zeta))
+                out[bi, h, lo:hi] = mag * dphi(q[bi, h, lo:hi])
+    return out
+
+
 def backward(q, k, v, cls, b, d_o, scale=None, branches=("softmax", "linear")):
     """dQ, dK, dV (float64 [B, H, N, d]) of sum(O * d_o) with O from sla.forward.
 

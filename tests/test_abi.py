@@ -99,6 +99,15 @@ def test_workspace_sizes(mod):
     # aligned), fp32 zeta_i [8, 128], bf16 gathered S_i^T [8, 128*128]
     assert lib.sla_linear_branch_ws_bytes(1, 1, 1000, 128, 128) == \
         8 * 128 * 128 * 2 + 8 * 128 * 4 + 256 + 8 * 128 * 4 + 8 * 128 * 128 * 2
+    # backward, every shape: D fp32 [2, 1024], column bits [2, 16, 2 words],
+    # counts [2, 16], uint16 column lists [2, 16, 16] (each piece 256-byte aligned)
+    for d, b in ((64, 64), (128, 64)):
+        assert lib.sla_sparse_attn_bwd_ws_bytes(1, 2, 1024, d, b) == 8192 + 256 + 256 + 1024
+    # linear backward: dS_i and dH_j bf16 [2, 16, d*d], dzeta_i and dz_j fp32 [2, 16, d],
+    # column bits [2, 16, 2 words]
+    assert lib.sla_linear_branch_bwd_ws_bytes(1, 2, 1024, 64, 64) == \
+        2 * (2 * 16 * 64 * 64 * 2) + 2 * (2 * 16 * 64 * 4) + 256
+    assert lib.sla_linear_branch_bwd_ws_bytes(1, 2, 1024, 96, 64) == 0
 
 
 def test_other_entry_points_reject_bad_arguments(mod):

@@ -37,6 +37,22 @@ def _grad_close(got, want, what, rel_l2=REL_L2):
     return check_close(got, want, what, max_abs=MAX_ABS * scale, rel_l2=rel_l2)
 
 
+# The linear branch's dQ is the difference of two terms that nearly cancel
+# (oracle.grad.linear_dq_scale), and S_i and g enter the MFMA in bf16: each
+# rounding is at most 2^-9 of a term, so the error of dQ is measured against
+# the size of the terms: |got - ref|_2 <= 5e-3 |ref|_2 + 2^-9 |terms|_2.
+LIN_TERM_BAR = 2.0 ** -9
+
+
+def _dq_close(got, want, terms, what):
+    err = float(np.linalg.norm(got - want))
+    ref, size = float(np.linalg.norm(want)), float(np.linalg.norm(terms))
+    say(f"  {what}: |err| = {err:.3e}, |ref| = {ref:.3e}, |terms| = {size:.3e}, "
+        f"|err| / |terms| = {err / max(size, 1e-30):.3e}")
+    _grad_close(got, want, what, rel_l2=np.inf)  # the max-abs bar
+    assert err <= REL_L2 * ref + LIN_TERM_BAR * size, f"{what}: {err} > bar"
+
+
 def _mask(nb, H, seed, dense_frac=0.35):
     g = np.random.default_rng(seed)
     cls = np.where(g.random((1, H, nb, nb)) < dense_frac, osla.CRITICAL, osla.SKIP).astype(np.uint8)
@@ -154,21 +170,40 @@ def _run_both(spec, cls, branches, seed=9):
     torch.cuda.synchronize()
     q64, k64, v64, do64 = (osla.bf16_to_f64(x) for x in (data["q"], data["k"], data["v"], do_bits))
     ref = ograd.backward(q64, k64, v64, cls, b, do64, branches=branches)
-    return (dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()), ref
+    terms = ograd.linear_dq_scale(q64, k64, v64, cls, b, do64)
+    return (dq.cpu().numpy(), dk.cpu().numpy(), dv.cpu().numpy()), ref, terms
 
 
 def test_linear_backward_small():
     say("[backward] linear branch alone, N=1000 (ragged)")
     cls = _mask3(SPEC.nb, SPEC.H, 21)
-    got, ref = _run_both(SPEC, cls, ("linear",))
-    # The linear branch's dQ is (S_i - zeta_i O_lin^T) g: two terms that largely
-    # cancel, each carrying the bf16 rounding of S_i (2^-9 relative), so its
-    # relative error is 2^-9 times the cancellation factor: its rel-L2 bar is
-    # doubled.  dK and dV have no such difference.
-    for a, b, n, rel in zip(got, ref, ("dQ", "dK", "dV"), (2 * REL_L2, REL_L2, REL_L2)):
-        _grad_close(a, b, n, rel_l2=rel)
+    got, ref, terms = _run_both(SPEC, cls, ("linear",))
+    # dK and dV have no cancelling difference: the plain bars
+    _dq_close(got[0], ref[0], terms, "dQ")
+    for a, b, n in zip(got[1:], ref[1:], ("dK", "dV")):
+        _grad_close(a, b, n)
     assert not got[1][0, 1, 4 * 128:5 * 128].any() and not got[2][0, 1, 4 * 128:5 * 128].any()
     assert not got[0][0, 0, 128:256].any() and not got[0][0, 1, 3 * 128:4 * 128].any()
+
+
+@pytest.mark.parametrize("d,block", [(64, 64), (64, 128), (128, 64)])
+def test_linear_backward_other_shapes(d, block):
+    """The generic linear-branch kernels, alone and after the softmax branch."""
+    N = 1000
+    spec = Spec(305, f"lbwd_d{d}_b{block}", B=1, H=2, N=N, d=d, block=block, kind="fourier",
+                grid=(10, 10, 10), mode="topk", keep=F(1, 2))
+    say(f"[backward] linear branch, d={d}, block={block}, N={N}")
+    cls = _mask3(spec.nb, spec.H, 23)
+    got, ref, terms = _run_both(spec, cls, ("linear",))
+    _dq_close(got[0], ref[0], terms, "dQ")
+    for a, b, n in zip(got[1:], ref[1:], ("dK", "dV")):
+        _grad_close(a, b, n)
+    assert not got[1][0, 1, 4 * block:5 * block].any() and not got[2][0, 1, 4 * block:5 * block].any()
+    assert not got[0][0, 0, block:2 * block].any() and not got[0][0, 1, 3 * block:4 * block].any()
+    got, ref, terms = _run_both(spec, cls, ("softmax", "linear"))
+    _dq_close(got[0], ref[0], terms, "dQ (both)")
+    for a, b, n in zip(got[1:], ref[1:], ("dK", "dV")):
+        _grad_close(a, b, f"{n} (both)")
 
 
 def test_both_branches_backward():
@@ -176,8 +211,9 @@ def test_both_branches_backward():
                 grid=(10, 10, 29), mode="topk", keep=F(1, 2))
     say("[backward] both branches, N=2900 (ragged), sparse then linear accumulating")
     cls = _mask3(spec.nb, spec.H, 22)
-    got, ref = _run_both(spec, cls, ("softmax", "linear"))
-    for a, b, n in zip(got, ref, ("dQ", "dK", "dV")):
+    got, ref, terms = _run_both(spec, cls, ("softmax", "linear"))
+    _dq_close(got[0], ref[0], terms, "dQ")
+    for a, b, n in zip(got[1:], ref[1:], ("dK", "dV")):
         _grad_close(a, b, n)
 
 

@@ -126,3 +126,31 @@ def test_empty_rows_get_no_gradient():
 def test_dphi_closed_form():
     x = np.array([-3.0, -0.5, 0.0, 1e-12, 2.0])
     np.testing.assert_allclose(grad.dphi(x), [math.exp(-3.0), math.exp(-0.5), 1.0, 1.0, 1.0])
+
+
+def test_linear_dq_scale_bounds_and_closed_form():
+    """The size of the linear dQ's terms bounds |dQ| (triangle inequality), and
+    with every value row the same vector c the two terms cancel exactly: dQ = 0
+    while the size is zeta (|dO| . |c| + |dO . c|) phi'(q) / w."""
+    q, k, v, d_o, cls, b = _case(41)
+    dq, _, _ = grad.backward(q, k, v, cls, b, d_o, branches=("linear",))
+    scale = grad.linear_dq_scale(q, k, v, cls, b, d_o)
+    assert (np.abs(dq) <= scale * (1 + 1e-12) + 1e-15).all()
+    assert scale[0, 0, 8:16].min() > 0                    # a fully marginal block
+    assert not scale[0, 0, 16:24].any()                   # a block with no marginal tile
+
+    g = np.random.default_rng(42)
+    N, d, bb = 20, 3, 4
+    q1, k1, d1 = (g.normal(size=(1, 1, N, d)) for _ in range(3))
+    c = g.normal(size=d)
+    v1 = np.broadcast_to(c, (1, 1, N, d)).copy()
+    cls1 = np.full((1, 1, 5, 5), sla.MARGINAL, dtype=np.uint8)
+    dq1, _, _ = grad.backward(q1, k1, v1, cls1, bb, d1, branches=("linear",))
+    sc1 = grad.linear_dq_scale(q1, k1, v1, cls1, bb, d1)
+    a = sla.phi(q1[0, 0])
+    zeta = sla.phi(k1[0, 0]).sum(axis=0)
+    w = a @ zeta
+    want = zeta[None, :] * ((np.abs(d1[0, 0]) @ np.abs(c)) + np.abs(d1[0, 0] @ c))[:, None] \
+        / w[:, None] * grad.dphi(q1[0, 0])
+    assert np.allclose(sc1[0, 0], want, rtol=1e-12, atol=0)
+    assert np.abs(dq1).max() < 1e-12 * sc1.max()
