@@ -20,6 +20,7 @@
 //       dV^T += dO^T P, dK^T += Q^T dS.
 #include "common.h"
 #include "launch.h"
+#include "staging.h"
 
 namespace sla {
 namespace gbwd {

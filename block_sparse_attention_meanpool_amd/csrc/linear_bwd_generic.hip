@@ -14,6 +14,7 @@
 // into.
 #include "common.h"
 #include "launch.h"
+#include "staging.h"
 #include "linear_apply.h"
 
 namespace sla {
