@@ -62,55 +62,64 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Scores: S[bh][i][j] = scale * qbar_i . kbar_j in fp32.  64x64 output tile
-// per workgroup, 256 threads with 4x4 outputs each, features staged through
-// LDS in slices of 32.
+// Scores: S[bh][i][j] = scale * qbar_i . kbar_j in fp32, each dot product one
+// fmaf chain in feature order.  128x128 output tile per workgroup, 256 threads
+// with 8x8 outputs each (rows 8*ti.., columns 8*tj..), features staged through
+// LDS in slices of 16; a thread's 8 row and 8 column operands are two 16-byte
+// LDS reads each.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qp,
                                                     const float* __restrict__ kp,
                                                     float* __restrict__ S, int nb, float scale) {
-  constexpr int TS = 64, KS = 32;
-  __shared__ float qs[KS][TS + 4];
-  __shared__ float ks[KS][TS + 4];
+  constexpr int TS = 128, KS = 16;
+  __shared__ __attribute__((aligned(16))) float qs[KS][TS];
+  __shared__ __attribute__((aligned(16))) float ks[KS][TS];
   const int64_t bh = blockIdx.z;
   const int i0 = blockIdx.y * TS, j0 = blockIdx.x * TS;
   const float* qh = qp + bh * nb * D;
   const float* kh = kp + bh * nb * D;
   const int t = threadIdx.x;
   const int ti = t / 16, tj = t % 16;
-  float acc[4][4] = {};
+  float acc[8][8] = {};
   for (int f0 = 0; f0 < D; f0 += KS) {
-    // 64 rows x 32 features per operand = 2048 floats, 8 per thread.
+    // 128 rows x 16 features per operand = 2048 floats, 8 per thread, read as
+    // 4 consecutive features of one row (16 bytes).
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      int idx = t + 256 * e;
-      int row = idx / KS, f = idx % KS;
-      int gi = i0 + row, gj = j0 + row;
-      qs[f][row] = gi < nb ? qh[(int64_t)gi * D + f0 + f] : 0.f;
-      ks[f][row] = gj < nb ? kh[(int64_t)gj * D + f0 + f] : 0.f;
+    for (int e = 0; e < 2; ++e) {
+      const int idx = t + 256 * e;  // 0..511: row idx / 4, features 4 * (idx % 4)
+      const int row = idx / 4, f = 4 * (idx % 4);
+      const int gi = i0 + row, gj = j0 + row;
+      const f32x4 a = gi < nb ? *(const f32x4*)(qh + (int64_t)gi * D + f0 + f) : f32x4{};
+      const f32x4 b = gj < nb ? *(const f32x4*)(kh + (int64_t)gj * D + f0 + f) : f32x4{};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        qs[f + u][row] = a[u];
+        ks[f + u][row] = b[u];
+      }
     }
     __syncthreads();
-#pragma unroll 8
+#pragma unroll 4
     for (int f = 0; f < KS; ++f) {
-      float a[4], b[4];
+      const f32x4 a0 = *(const f32x4*)&qs[f][8 * ti], a1 = *(const f32x4*)&qs[f][8 * ti + 4];
+      const f32x4 b0 = *(const f32x4*)&ks[f][8 * tj], b1 = *(const f32x4*)&ks[f][8 * tj + 4];
+      const float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+      const float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) { a[u] = qs[f][ti + 16 * u]; b[u] = ks[f][tj + 16 * u]; }
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int w = 0; w < 4; ++w) acc[u][w] = fmaf(a[u], b[w], acc[u][w]);
+        for (int w = 0; w < 8; ++w) acc[u][w] = fmaf(a[u], b[w], acc[u][w]);
     }
     __syncthreads();
   }
   float* Sh = S + bh * (int64_t)nb * nb;
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    int gi = i0 + ti + 16 * u;
+  for (int u = 0; u < 8; ++u) {
+    const int gi = i0 + 8 * ti + u;
     if (gi >= nb) continue;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      int gj = j0 + tj + 16 * w;
+    for (int w = 0; w < 8; ++w) {
+      const int gj = j0 + 8 * tj + w;
       if (gj < nb) Sh[(int64_t)gi * nb + gj] = scale * acc[u][w];
     }
   }
@@ -121,7 +130,8 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qp
 // j = lane + 64*t as 44-bit keys (order-preserving fp32 bits << 12 |
 // 4095 - j), so that a larger key means "earlier in the descending order,
 // ties to the lower j".  All keys are distinct, and a bit-by-bit search finds
-//   - the k-th largest key (top-k and the two cuts of the three-way split);
+//   - a threshold that admits exactly the k largest keys (top-k and the two
+//     cuts of the three-way split);
 //   - the largest key T whose prefix {key >= T} holds softmax mass >= 1 - thr
 //     (the NABLA cut), which is exactly the smallest such prefix.
 // ---------------------------------------------------------------------------
@@ -147,6 +157,10 @@ __device__ __forceinline__ float wave_max_f(float x) {
   return x;
 }
 
+// A threshold T with exactly k keys >= T.  The search fixes bits from the
+// top while at least k keys stay above the candidate; once exactly k do, the
+// candidate already separates the k largest from the rest (the same set the
+// k-th largest key itself would select), so the remaining bits are skipped.
 template <int MC>
 __device__ __forceinline__ uint64_t kth_largest(const uint64_t (&key)[MC], int n_here, int k) {
   uint64_t T = 0;
@@ -155,7 +169,11 @@ __device__ __forceinline__ uint64_t kth_largest(const uint64_t (&key)[MC], int n
     int c = 0;
 #pragma unroll
     for (int t = 0; t < MC; ++t) c += (t < n_here && key[t] >= cand) ? 1 : 0;
-    if (wave_sum_i(c) >= k) T = cand;
+    c = wave_sum_i(c);
+    if (c >= k) {
+      T = cand;
+      if (c == k) break;
+    }
   }
   return T;
 }
@@ -235,7 +253,7 @@ hipError_t launch_pool(const uint16_t* q, const uint16_t* k, float* qp, float* k
 
 hipError_t launch_scores(const float* qp, const float* kp, float* S, int64_t BH, int d, int nb,
                          float scale, hipStream_t s) {
-  dim3 grid((nb + 63) / 64, (nb + 63) / 64, (unsigned)BH);
+  dim3 grid((nb + 127) / 128, (nb + 127) / 128, (unsigned)BH);
   if (d == 128) score_kernel<128><<<grid, 256, 0, s>>>(qp, kp, S, nb, scale);
   else score_kernel<64><<<grid, 256, 0, s>>>(qp, kp, S, nb, scale);
   return hipGetLastError();
