@@ -368,7 +368,7 @@ def main():
                                 "what": "share of each query's dense softmax mass on its critical tiles"}
         del rec
 
-    if not args.no_backward and d == 128 and b == 128:
+    if not args.no_backward:
         extra["backward"] = backward_timing(sla, torch, q, k, v, b, crit_idx, crit_cnt, marg_idx,
                                             marg_cnt, km, flop, args.steps, stream)
         log(f"[bench] backward: {extra['backward']}")

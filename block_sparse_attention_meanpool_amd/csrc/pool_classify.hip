@@ -63,16 +63,16 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
 
 // ---------------------------------------------------------------------------
 // Scores: S[bh][i][j] = scale * qbar_i . kbar_j in fp32, each dot product one
-// fmaf chain in feature order.  128x128 output tile per workgroup, 256 threads
-// with 8x8 outputs each (rows 8*ti.., columns 8*tj..), features staged through
-// LDS in slices of 16; a thread's 8 row and 8 column operands are two 16-byte
-// LDS reads each.
+// fmaf chain in feature order.  TS x TS output tile per workgroup (TS = 64 or
+// 128), 256 threads with R x R outputs each (R = TS / 16; rows R*ti..,
+// columns R*tj..), features staged through LDS in slices of 16; a thread's R
+// row and R column operands are 16-byte LDS reads.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int TS>
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qp,
                                                     const float* __restrict__ kp,
                                                     float* __restrict__ S, int nb, float scale) {
-  constexpr int TS = 128, KS = 16;
+  constexpr int KS = 16, R = TS / 16, LD = TS / 64;
   __shared__ __attribute__((aligned(16))) float qs[KS][TS];
   __shared__ __attribute__((aligned(16))) float ks[KS][TS];
   const int64_t bh = blockIdx.z;
@@ -81,13 +81,13 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qp
   const float* kh = kp + bh * nb * D;
   const int t = threadIdx.x;
   const int ti = t / 16, tj = t % 16;
-  float acc[8][8] = {};
+  float acc[R][R] = {};
   for (int f0 = 0; f0 < D; f0 += KS) {
-    // 128 rows x 16 features per operand = 2048 floats, 8 per thread, read as
-    // 4 consecutive features of one row (16 bytes).
+    // TS rows x 16 features per operand, read as 4 consecutive features of
+    // one row (16 bytes), LD reads per thread and operand.
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int idx = t + 256 * e;  // 0..511: row idx / 4, features 4 * (idx % 4)
+    for (int e = 0; e < LD; ++e) {
+      const int idx = t + 256 * e;  // row idx / 4, features 4 * (idx % 4)
       const int row = idx / 4, f = 4 * (idx % 4);
       const int gi = i0 + row, gj = j0 + row;
       const f32x4 a = gi < nb ? *(const f32x4*)(qh + (int64_t)gi * D + f0 + f) : f32x4{};
@@ -101,25 +101,32 @@ __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qp
     __syncthreads();
 #pragma unroll 4
     for (int f = 0; f < KS; ++f) {
-      const f32x4 a0 = *(const f32x4*)&qs[f][8 * ti], a1 = *(const f32x4*)&qs[f][8 * ti + 4];
-      const f32x4 b0 = *(const f32x4*)&ks[f][8 * tj], b1 = *(const f32x4*)&ks[f][8 * tj + 4];
-      const float a[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
-      const float b[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+      float a[R], b[R];
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int v = 0; v < R / 4; ++v) {
+        const f32x4 av = *(const f32x4*)&qs[f][R * ti + 4 * v];
+        const f32x4 bv = *(const f32x4*)&ks[f][R * tj + 4 * v];
 #pragma unroll
-        for (int w = 0; w < 8; ++w) acc[u][w] = fmaf(a[u], b[w], acc[u][w]);
+        for (int u = 0; u < 4; ++u) {
+          a[4 * v + u] = av[u];
+          b[4 * v + u] = bv[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < R; ++u)
+#pragma unroll
+        for (int w = 0; w < R; ++w) acc[u][w] = fmaf(a[u], b[w], acc[u][w]);
     }
     __syncthreads();
   }
   float* Sh = S + bh * (int64_t)nb * nb;
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int gi = i0 + 8 * ti + u;
+  for (int u = 0; u < R; ++u) {
+    const int gi = i0 + R * ti + u;
     if (gi >= nb) continue;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const int gj = j0 + 8 * tj + w;
+    for (int w = 0; w < R; ++w) {
+      const int gj = j0 + R * tj + w;
       if (gj < nb) Sh[(int64_t)gi * nb + gj] = scale * acc[u][w];
     }
   }
@@ -253,9 +260,18 @@ hipError_t launch_pool(const uint16_t* q, const uint16_t* k, float* qp, float* k
 
 hipError_t launch_scores(const float* qp, const float* kp, float* S, int64_t BH, int d, int nb,
                          float scale, hipStream_t s) {
-  dim3 grid((nb + 127) / 128, (nb + 127) / 128, (unsigned)BH);
-  if (d == 128) score_kernel<128><<<grid, 256, 0, s>>>(qp, kp, S, nb, scale);
-  else score_kernel<64><<<grid, 256, 0, s>>>(qp, kp, S, nb, scale);
+  // 128 x 128 tiles when they still give two workgroups per CU (256 CUs),
+  // else 64 x 64 tiles for more parallelism
+  const int64_t t128 = (int64_t)((nb + 127) / 128) * ((nb + 127) / 128) * BH;
+  if (t128 >= 512) {
+    const dim3 grid((nb + 127) / 128, (nb + 127) / 128, (unsigned)BH);
+    if (d == 128) score_kernel<128, 128><<<grid, 256, 0, s>>>(qp, kp, S, nb, scale);
+    else score_kernel<64, 128><<<grid, 256, 0, s>>>(qp, kp, S, nb, scale);
+  } else {
+    const dim3 grid((nb + 63) / 64, (nb + 63) / 64, (unsigned)BH);
+    if (d == 128) score_kernel<128, 64><<<grid, 256, 0, s>>>(qp, kp, S, nb, scale);
+    else score_kernel<64, 64><<<grid, 256, 0, s>>>(qp, kp, S, nb, scale);
+  }
   return hipGetLastError();
 }
 
