@@ -24,9 +24,11 @@
 namespace sla {
 
 // LIST: key tiles from the per-query-block lists (sparse); otherwise every
-// tile in order (the dense baseline, a separate instantiation).
+// tile in order (the dense baseline, a separate instantiation).  d = 64 fits
+// three waves per SIMD without spills (a quarter faster than two); d = 128
+// keeps two.
 template <int D, int BLK, bool LIST>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_fwd_kernel(
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2, D == 64 ? 3 : 2))) void attn_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse, int seg,
