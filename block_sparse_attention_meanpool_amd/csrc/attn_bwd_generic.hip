@@ -34,8 +34,11 @@ __device__ __forceinline__ void stage(const __amdgpu_buffer_rsrc_t& r, int row0,
   stage_subblocks<BLK, D, BLK * 2>(r, row0, rows, tr, tid, KeepChunk{});
 }
 
+// d = 64 with 64-token blocks fits three waves per SIMD without spills (10%
+// faster than two); the other shapes keep two.
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void dq_kernel(
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(
+    D == 64 && BLK == 64 ? 3 : 2, D == 64 && BLK == 64 ? 3 : 2))) void dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const void* __restrict__ o_s, int o_fp32, const float* __restrict__ lse,
     const uint16_t* __restrict__ d_o, int N, int nqb, int nkb, const int32_t* __restrict__ idx,
