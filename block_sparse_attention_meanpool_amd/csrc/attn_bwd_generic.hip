@@ -176,8 +176,10 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+// Two waves per SIMD where the registers allow it; d = 128 (its dK and dV
+// accumulators alone take 128 registers) runs at one.
 template <int D, int BLK>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void dkdv_kernel(
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(D == 128 ? 1 : 2, 2))) void dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ lse, const float* __restrict__ Dbuf,
     const uint16_t* __restrict__ d_o, int N, int nqb, int nkb,
