@@ -206,6 +206,26 @@ def test_linear_backward_other_shapes(d, block):
         _grad_close(a, b, f"{n} (both)")
 
 
+@pytest.mark.parametrize("d,block", [(128, 128), (64, 64)])
+def test_backward_two_batches(d, block):
+    """B = 2: every kernel indexes batch and head as one flattened dimension."""
+    N = 700
+    spec = Spec(306, f"bwd_b2_d{d}_b{block}", B=2, H=2, N=N, d=d, block=block, kind="fourier",
+                grid=(7, 10, 10), mode="topk", keep=F(1, 2))
+    say(f"[backward] both branches, B=2, d={d}, block={block}, N={N}")
+    g = np.random.default_rng(24)
+    nb = spec.nb
+    cls = g.choice(np.array([osla.SKIP, osla.MARGINAL, osla.CRITICAL], dtype=np.uint8),
+                   size=(2, spec.H, nb, nb), p=[0.4, 0.35, 0.25])
+    cls[1, 1, 0] = osla.CRITICAL  # a row of the second batch with every tile critical
+    cls[1, 0, 1] = osla.SKIP      # and one with nothing
+    got, ref, terms = _run_both(spec, cls, ("softmax", "linear"))
+    _dq_close(got[0], ref[0], terms, "dQ")
+    for a, b, n in zip(got[1:], ref[1:], ("dK", "dV")):
+        _grad_close(a, b, n)
+    assert not got[0][1, 0, block:2 * block].any()
+
+
 def test_both_branches_backward():
     spec = Spec(303, "bwd_sla3", B=1, H=2, N=2900, d=128, block=128, kind="fourier",
                 grid=(10, 10, 29), mode="topk", keep=F(1, 2))
