@@ -50,7 +50,6 @@ def log(*a):
 def kept_flop(crit_idx, crit_cnt, N, block, d):
     """Exact kept-pair FLOP: 4 * rows(i) * keys(j) * d over every kept pair."""
     import torch
-    nb = crit_idx.shape[-1]
     width = crit_idx.shape[-1]
     nqb = crit_idx.shape[-2]
     valid = torch.arange(width, device=crit_idx.device) < crit_cnt[..., None]
@@ -59,8 +58,20 @@ def kept_flop(crit_idx, crit_cnt, N, block, d):
     keys = torch.where(valid, keys, torch.zeros_like(keys))
     rows = torch.clamp(N - torch.arange(nqb, device=j.device) * block, max=block)
     per = (keys.sum(-1) * rows).sum().item()
-    del nb
     return 4.0 * per * d
+
+
+def pipe_mfma_flop(crit_idx, crit_cnt, N):
+    """MFMA FLOP the d = 128, 128-token kernel issues for these lists: every
+    kept tile runs its first 64-key half, and its second when that half holds
+    a key below N; a half is 4 waves x 32 MFMAs of 32x32x16 (32768 FLOP), over
+    all 128 rows of the query block (the rows past N of the last block too)."""
+    import torch
+    width = crit_idx.shape[-1]
+    valid = torch.arange(width, device=crit_idx.device) < crit_cnt[..., None]
+    j = torch.where(valid, crit_idx, torch.zeros_like(crit_idx)).long()
+    halves = torch.where(valid, 1 + (j * 128 + 64 < N).long(), torch.zeros_like(j))
+    return float(halves.sum().item()) * 4 * 32 * 32768
 
 
 # Sources of the sparse-attention kernel; a counter summary applies only to the
@@ -211,6 +222,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--profile", action="store_true", help="short run for a profiler")
+    ap.add_argument("--profile-dense", action="store_true",
+                    help="with --profile: one dense-kernel launch after the copy")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--unfused", action="store_true",
                     help="with a linear branch: separate sparse, linear and combine calls")
@@ -326,6 +339,20 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+        if d == 128 and b == 128:
+            log(f"[bench] expected MFMA FLOP per sparse launch: "
+                f"{pipe_mfma_flop(crit_idx, crit_cnt, N) * B:.6e}")
+        if args.profile_dense:
+            od = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+            sla.sla_dense_attn_fwd(q, k, v, b, o=od)
+            torch.cuda.synchronize()
+            if d == 128 and b == 128:
+                every = torch.arange(nb, dtype=torch.int32, device=dev).expand(B, H, nb, nb)
+                full = torch.full((B, H, nb), nb, dtype=torch.int32, device=dev)
+                log(f"[bench] expected MFMA FLOP per dense launch: "
+                    f"{pipe_mfma_flop(every, full, N) * B:.6e} "
+                    f"(attention FLOP 4*H*N*N*d: {4.0 * B * H * N * N * d:.6e})")
+            del od
 
     flop = kept_flop(crit_idx, crit_cnt, N, b, d) * B
     kept_frac = crit_cnt.double().mean().item() / nb
