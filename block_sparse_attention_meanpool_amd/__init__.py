@@ -5,17 +5,17 @@ include/sla.h); this package is its Python binding.
 """
 
 from .binding import (CLS_CRITICAL, CLS_MARGINAL, CLS_SKIP, EXPORTS, FLAG_BAD_CLASS, FLAG_OVERFLOW,
-                      LIB_PATH, MODES, SlaError, count_from_fraction, counts_for, forward, lib,
-                      num_blocks, sla_block_mask, sla_combine, sla_dense_attn_fwd,
-                      sla_linear_branch_bwd, sla_linear_branch_fwd, sla_linear_branch_prepare,
-                      sla_mask_recall, sla_pool_classify,
+                      LIB_PATH, MODES, SlaAttention, SlaError, count_from_fraction, counts_for,
+                      forward, lib, num_blocks, sla_attention, sla_block_mask, sla_combine,
+                      sla_dense_attn_fwd, sla_linear_branch_bwd, sla_linear_branch_fwd,
+                      sla_linear_branch_prepare, sla_mask_recall, sla_pool_classify,
                       sla_sparse_attn_bwd, sla_sparse_attn_fwd, sla_sparse_linear_attn_fwd,
                       sla_status_string, sla_tile_permute, sla_version)
 
 __all__ = ["CLS_CRITICAL", "CLS_MARGINAL", "CLS_SKIP", "EXPORTS", "FLAG_BAD_CLASS", "FLAG_OVERFLOW",
-           "LIB_PATH", "MODES", "SlaError", "count_from_fraction", "counts_for", "forward", "lib",
-           "num_blocks", "sla_block_mask", "sla_combine", "sla_dense_attn_fwd",
-           "sla_linear_branch_bwd", "sla_linear_branch_fwd", "sla_linear_branch_prepare",
-           "sla_mask_recall", "sla_pool_classify",
+           "LIB_PATH", "MODES", "SlaAttention", "SlaError", "count_from_fraction", "counts_for",
+           "forward", "lib", "num_blocks", "sla_attention", "sla_block_mask", "sla_combine",
+           "sla_dense_attn_fwd", "sla_linear_branch_bwd", "sla_linear_branch_fwd",
+           "sla_linear_branch_prepare", "sla_mask_recall", "sla_pool_classify",
            "sla_sparse_attn_bwd", "sla_sparse_attn_fwd", "sla_sparse_linear_attn_fwd",
            "sla_status_string", "sla_tile_permute", "sla_version"]

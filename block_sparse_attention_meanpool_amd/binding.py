@@ -356,17 +356,9 @@ def sla_combine(o_s, o_lin=None, o=None, stream=None):
 # the whole path
 # ---------------------------------------------------------------------------
 
-def forward(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=None, o_fp32=False,
-            fused=False, stream=None):
-    """Pool and classify (unless `cls` is given: mask-in), compact the lists,
-    run the sparse and linear branches and combine.  With fused=True and a
-    linear branch, the two branches run as sla_linear_branch_prepare plus
-    sla_sparse_linear_attn_fwd (no O_s / O_lin intermediates).
-
-    mode "topk" (keep), "cdf" (thr), "sla3" (keep, marg).  With a given cls,
-    `keep`/`marg` only size the lists (default: the whole row).
-    Returns a dict with o (bf16 [B, H, N, d]) and every intermediate.
-    """
+def _select(q, k, block, mode, keep, marg, thr, cls, stream):
+    """Class map (pooled and classified, unless given) and its compacted lists;
+    the marginal lists are None when the selection has no marginal tiles."""
     B, H, N, d = q.shape
     nb = num_blocks(N, block)
     if cls is None:
@@ -380,6 +372,23 @@ def forward(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=Non
         km_max = (counts_for("sla3", nb, keep, marg)[1] if keep is not None and marg is not None
                   else nb)
     crit_idx, crit_cnt, marg_idx, marg_cnt = sla_block_mask(cls, kc_max, km_max, stream=stream)
+    return cls, crit_idx, crit_cnt, marg_idx, marg_cnt
+
+
+def forward(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=None, o_fp32=False,
+            fused=False, stream=None):
+    """Pool and classify (unless `cls` is given: mask-in), compact the lists,
+    run the sparse and linear branches and combine.  With fused=True and a
+    linear branch, the two branches run as sla_linear_branch_prepare plus
+    sla_sparse_linear_attn_fwd (no O_s / O_lin intermediates).
+
+    mode "topk" (keep), "cdf" (thr), "sla3" (keep, marg).  With a given cls,
+    `keep`/`marg` only size the lists (default: the whole row).
+    Returns a dict with o (bf16 [B, H, N, d]) and every intermediate.
+    """
+    cls, crit_idx, crit_cnt, marg_idx, marg_cnt = _select(q, k, block, mode, keep, marg, thr, cls,
+                                                          stream)
+    km_max = 0 if marg_idx is None else marg_idx.shape[-1]
     out = {"cls": cls, "crit_idx": crit_idx, "crit_cnt": crit_cnt, "marg_idx": marg_idx,
            "marg_cnt": marg_cnt}
     if km_max and fused:
@@ -398,3 +407,55 @@ def forward(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=Non
         o, _ = sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, o_fp32=False, stream=stream)
         out.update(o=o)
     return out
+
+
+# ---------------------------------------------------------------------------
+# training: the path as a torch.autograd.Function
+# ---------------------------------------------------------------------------
+
+class SlaAttention(torch.autograd.Function):
+    """O = sparse softmax attention over the critical tiles plus linear
+    attention over the marginal tiles (bf16), differentiable in q, k and v
+    with the lists held fixed.  Forward: sla_sparse_attn_fwd (fp32 O_s and
+    LSE kept for the backward), sla_linear_branch_fwd, sla_combine.  Backward:
+    sla_sparse_attn_bwd, then sla_linear_branch_bwd adds the linear branch's
+    gradients; they are fp32, and autograd rounds them to the inputs' bf16.
+    marg_idx / marg_cnt may be None (no linear branch)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, block, crit_idx, crit_cnt, marg_idx=None, marg_cnt=None):
+        o_s, lse = sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, o_fp32=True,
+                                       want_lse=True)
+        lin_ws = None
+        o_lin = None
+        if marg_idx is not None:
+            B, H, N, d = q.shape
+            lin_ws = torch.empty(max(lib().sla_linear_branch_ws_bytes(B, H, N, d, block), 1),
+                                 dtype=torch.uint8, device=q.device)
+            o_lin = sla_linear_branch_fwd(q, k, v, block, marg_idx, marg_cnt, ws=lin_ws)
+        o = sla_combine(o_s, o_lin)
+        ctx.block = block
+        ctx.save_for_backward(q, k, v, crit_idx, crit_cnt, marg_idx, marg_cnt, o_s, lse, lin_ws)
+        return o
+
+    @staticmethod
+    def backward(ctx, d_o):
+        q, k, v, crit_idx, crit_cnt, marg_idx, marg_cnt, o_s, lse, lin_ws = ctx.saved_tensors
+        if d_o.dtype != torch.bfloat16:
+            raise ValueError(f"the output gradient must be bf16, got {d_o.dtype}")
+        d_o = d_o.contiguous()
+        dq, dk, dv = sla_sparse_attn_bwd(q, k, v, ctx.block, crit_idx, crit_cnt, o_s, lse, d_o)
+        if marg_idx is not None:
+            sla_linear_branch_bwd(q, k, v, ctx.block, marg_idx, marg_cnt, d_o, lin_ws, dq, dk, dv)
+        return dq, dk, dv, None, None, None, None, None
+
+
+def sla_attention(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=None,
+                  stream=None):
+    """Selection (no gradient) followed by SlaAttention: the differentiable
+    form of forward().  Returns (o, lists) with lists = (cls, crit_idx,
+    crit_cnt, marg_idx, marg_cnt)."""
+    with torch.no_grad():
+        lists = _select(q.detach(), k.detach(), block, mode, keep, marg, thr, cls, stream)
+    _, crit_idx, crit_cnt, marg_idx, marg_cnt = lists
+    return SlaAttention.apply(q, k, v, block, crit_idx, crit_cnt, marg_idx, marg_cnt), lists
