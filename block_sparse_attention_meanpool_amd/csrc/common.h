@@ -124,18 +124,17 @@ __device__ __forceinline__ void transpose8x8(const u32x4 in[8], u32x4 out[8]) {
   }
 }
 
-// Sub-block s of a (T tokens x F features) tile -> (token chunk tc, feature
-// chunk fc).  Within each 8-lane group the token chunks differ and the feature
+// Sub-block s of a tile of T tokens (by any feature width) -> (token chunk tc,
+// feature chunk fc).  Within each 8-lane group the token chunks differ and the feature
 // chunk is shared, so each global load instruction reads 128 contiguous bytes
 // of 8 rows and the transposed LDS writes (row 8 fc + i, chunk tc) land on 8
 // (and, with the neighbouring group, 16) distinct bank groups.
-template <int T, int F>
+template <int T>
 __device__ __forceinline__ void subblock_coords(int s, int& tc, int& fc) {
   constexpr int TH = T / 64;  // groups of 8 token chunks
   const int lane = s & 63, w = s >> 6;
   tc = 8 * (w % TH) + (lane & 7);
   fc = 8 * (w / TH) + (lane >> 3);
-  (void)F;
 }
 
 

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void lin_state_kernel(const uint16_t* __restri
     const int s = s0 + tid;
     if (NSUB % NT == 0 || s < NSUB) {
       int tc, fc;
-      subblock_coords<BLK, D>(s, tc, fc);
+      subblock_coords<BLK>(s, tc, fc);
       u32x4 ink[8], inv[8], out[8];
 #pragma unroll
       for (int r = 0; r < 8; ++r) {

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(D == 64
         const int s = s0 + tid;
         if (NSUB % NT == 0 || s < NSUB) {
           int tc, fc;
-          subblock_coords<BLK, D>(s, tc, fc);
+          subblock_coords<BLK>(s, tc, fc);
           u32x4 in[8], out[8];
 #pragma unroll
           for (int r = 0; r < 8; ++r)
@@ -226,10 +226,6 @@ constexpr int D = 128, BLK = 128, HALF = 64, NT = 256;
 constexpr int ROWB = D * 2;              // bytes per K / V row
 constexpr int BUFB = HALF * ROWB;        // 16 KB per half tile
 
-__device__ __forceinline__ int v_swz(int r) { return trs_swz(r); }
-
-__device__ __forceinline__ void wait_vm0() { wait_vmcnt0(); }
-
 struct Ctx {
   __amdgpu_buffer_rsrc_t rk, rv;
   int N, nkb, lane, w;
@@ -247,7 +243,7 @@ __device__ __forceinline__ void issue_half(const Ctx& c, int j, int hh, char* kb
     const int row = 4 * inst + (c.lane >> 4);      // row within the half tile
     const int grow = min(jj * BLK + HALF * hh + row, c.N - 1);
     const int kch = (c.lane & 15) ^ row_swz<16>(row);
-    const int vch = (c.lane & 15) ^ v_swz(row);
+    const int vch = (c.lane & 15) ^ trs_swz(row);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rk, (lds_void_ptr)(kbuf + inst * 1024), 16,
                                              (uint32_t)(grow * D + kch * 8) * 2, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rv, (lds_void_ptr)(vbuf + inst * 1024), 16,
@@ -258,8 +254,7 @@ __device__ __forceinline__ void issue_half(const Ctx& c, int j, int hh, char* kb
 // One 64-key half: S^T = K Q^T, masking, online softmax, O^T += V^T P^T.
 __device__ __forceinline__ void compute_half(const char* kbuf, const char* vbuf, const u32x4 (&qf)[8],
                                              f32x16 (&oacc)[4], float& m_run, float& l_run,
-                                             int key0, int N, float sl2, int l32, int hf, int krow,
-                                             int lane) {
+                                             int key0, int N, float sl2, int hf, int krow, int lane) {
   f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
@@ -319,7 +314,6 @@ __device__ __forceinline__ void compute_half(const char* kbuf, const char* vbuf,
       oacc[db] = mfma32x32x16(tr_operand(vbuf, 16 * ks2, 32 * db, lane), pb[ks2], oacc[db]);
   }
   __builtin_amdgcn_iglp_opt(2);
-  (void)l32;
 }
 
 template <bool LIST>
@@ -373,16 +367,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     // with the loads of buffer 0
     const int j_next = (t + 1 < count) ? (LIST ? list[t + 1] : t + 1) : 0;
     // first half of tile j_cur, in buffer 0
-    wait_vm0();
+    wait_vmcnt0();
     __syncthreads();  // buffer 0 complete; every wave is done with buffer 1
     issue_half(c, j_cur, 1, K1, V1);
-    if (ok) compute_half(K0, V0, qf, oacc, m_run, l_run, j_cur * BLK, N, sl2, l32, hf, krow, lane);
+    if (ok) compute_half(K0, V0, qf, oacc, m_run, l_run, j_cur * BLK, N, sl2, hf, krow, lane);
     // second half, in buffer 1
-    wait_vm0();
+    wait_vmcnt0();
     __syncthreads();  // buffer 1 complete; every wave is done with buffer 0
     if (t + 1 < count) issue_half(c, j_next, 0, K0, V0);
     if (ok && j_cur * BLK + HALF < N)
-      compute_half(K1, V1, qf, oacc, m_run, l_run, j_cur * BLK + HALF, N, sl2, l32, hf, krow, lane);
+      compute_half(K1, V1, qf, oacc, m_run, l_run, j_cur * BLK + HALF, N, sl2, hf, krow, lane);
     j_cur = j_next;
   }
 

@@ -23,7 +23,7 @@ __device__ __forceinline__ void stage_subblocks(const __amdgpu_buffer_rsrc_t& rs
     const int s = s0 + tid;
     if (NSUB % NT == 0 || s < NSUB) {
       int tc, fc;
-      subblock_coords<R, F>(s, tc, fc);
+      subblock_coords<R>(s, tc, fc);
       u32x4 in[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e)
