@@ -206,11 +206,24 @@ def cpu_baseline(spec, data, kc, km, budget_s=20.0):
         blocks += len(rows)
         h += 1
     dt = time.perf_counter() - t0
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+    single = None
+    if spec.N * spec.H <= 4096:
+        # a workload small enough for the whole oracle forward on one BLAS thread
+        from threadpoolctl import threadpool_limits
+        q, k, v = (osla.bf16_to_f64(data[t]) for t in "qkv")
+        with threadpool_limits(1):
+            t1 = time.perf_counter()
+            cls, *_ = osla.class_map(q, k, spec.block, sel, spec.keep, spec.marg, spec.thr)
+            osla.forward(q, k, v, cls, spec.block)
+            single = time.perf_counter() - t1
+    out = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": (f"fp64 numpy oracle: pool + score + top-k class map of {h} head(s) in full, "
                        f"then masked softmax attention of {blocks} sampled query blocks "
-                       f"(128 per head); kept-block FLOP of those blocks / wall time "
+                       f"({min(spec.nb, 128)} per head); kept-block FLOP of those blocks / wall time "
                        f"({dt:.1f} s)")}
+    if single is not None:
+        out["single_core_full_forward_s"] = single
+    return out
 
 
 def main():
@@ -330,6 +343,7 @@ def main():
     ms_step = wall * 1e3 / args.steps
     stage_ms = {s: float(np.mean(ev[s])) for s in stages}
     stage_min = {s: float(np.min(ev[s])) for s in stages}
+    stage_med = {s: float(np.median(ev[s])) for s in stages}
     log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
 
     if args.profile:
@@ -361,7 +375,7 @@ def main():
     value = flop / (ms_step * 1e-3) / 1e12
     pool_bytes = 2 * B * H * N * d * 2 + 2 * B * H * nb * d * 4
     extra = {
-        "stage_ms_mean": stage_ms, "stage_ms_min": stage_min,
+        "stage_ms_mean": stage_ms, "stage_ms_median": stage_med, "stage_ms_min": stage_min,
         "kept_fraction": kept_frac, "kept_flop_per_step": flop,
         "sparse_kernel_tflops": achieved,
         "pool_classify_gbs_algorithmic": pool_bytes / (stage_ms["pool_classify"] * 1e-3) / 1e9,
