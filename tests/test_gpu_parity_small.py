@@ -34,6 +34,10 @@ SMALL = [
          grid=(4, 16, 16), mode="topk", keep=F(3, 8)),
     Spec(106, "cdf_d128_b128", B=1, H=2, N=1500, d=128, block=128, kind="fourier", grid=(5, 15, 20),
          mode="cdf", thr=0.1),
+    # two batches through the pipelined kernel, the linear branch and the fused path; the last
+    # block holds 60 tokens, so its second 64-key half is empty
+    Spec(107, "sla3_d128_b128_two_batches", B=2, H=2, N=700, d=128, block=128, kind="fourier",
+         grid=(7, 10, 10), mode="sla3", keep=F(2, 6), marg=F(2, 6)),
 ]
 
 
