@@ -20,6 +20,7 @@
 // as zeros.
 #include "common.h"
 #include "launch.h"
+#include "lists.h"
 
 namespace sla {
 namespace bwd {
@@ -270,11 +271,15 @@ __device__ __forceinline__ void issue_qhalf(const __amdgpu_buffer_rsrc_t& rq,
                                             const __amdgpu_buffer_rsrc_t& re, int row0, char* qbuf,
                                             char* obuf, float* lbuf, float* ebuf, int lane, int w) {
   issue_rows(rq, rdo, row0, qbuf, obuf, lane, w);
-  if (w < 2) {
-    const uint32_t off = (uint32_t)(row0 + lane) * 4;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(w == 0 ? rl : re,
-                                             (lds_void_ptr)(w == 0 ? lbuf : ebuf), 4, off, 0, 0, 0);
-  }
+  // The wave index is the same in every lane; taken through readfirstlane the
+  // compiler knows it, so descriptor and LDS destination stay scalar instead
+  // of being looped over lane by lane.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const uint32_t off = (uint32_t)(row0 + lane) * 4;
+  if (wu == 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void_ptr)lbuf, 4, off, 0, 0, 0);
+  else if (wu == 1)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void_ptr)ebuf, 4, off, 0, 0, 0);
 }
 
 // One 64-query half: for each 32-query block, S = Q K^T, dP = dO V^T,
@@ -351,8 +356,8 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(
   const __amdgpu_buffer_rsrc_t re = make_rsrc(Dbuf + bh * N, (uint32_t)N * 4);
 
   const int count = col_cnt[bh * nkb + kt];
-  const uint16_t* list = col_idx + (bh * nkb + kt) * (int64_t)width;
-  int i_cur = count > 0 ? list[0] : 0;
+  const int64_t list0 = (bh * nkb + kt) * (int64_t)width;  // first entry of this tile's list
+  int i_cur = count > 0 ? u16_entry(col_idx, list0) : 0;
   if (count > 0) issue_qhalf(rq, rdo, rl, re, i_cur * BLK, Q0, O0, L0, E0, lane, w);
 
   const int key = kt * BLK + 32 * w + l32;
@@ -367,7 +372,7 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(
   f32x16 dvacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   const int qrowp = swap_bits_2_3(l32);
   for (int t = 0; t < count; ++t) {
-    const int i_next = (t + 1 < count) ? list[t + 1] : 0;
+    const int i_next = (t + 1 < count) ? u16_entry(col_idx, list0 + t + 1) : 0;
     wait_vmcnt0();
     __syncthreads();  // buffer 0 complete; every wave is done with buffer 1
     issue_qhalf(rq, rdo, rl, re, i_cur * BLK + HALF, Q1, O1, L1, E1, lane, w);

@@ -20,6 +20,7 @@
 //       dV^T += dO^T P, dK^T += Q^T dS.
 #include "common.h"
 #include "launch.h"
+#include "lists.h"
 #include "staging.h"
 
 namespace sla {
@@ -220,10 +221,10 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(D == 12
   for (int db = 0; db < D / 32; ++db) dkacc[db] = dvacc[db] = f32x16{};
   const int qrowp = swap_bits_2_3(l32);
   const int count = col_cnt[bh * nkb + kt];
-  const uint16_t* list = col_idx + (bh * nkb + kt) * (int64_t)width;
+  const int64_t list0 = (bh * nkb + kt) * (int64_t)width;  // first entry of this tile's list
 
   for (int t = 0; t < count; ++t) {
-    const int i = list[t];
+    const int i = u16_entry(col_idx, list0 + t);
     __syncthreads();  // the previous block's LDS reads are done
     stage<D, BLK>(rq, i * BLK, Qs, Qt, tid);
     stage<D, BLK>(rdo, i * BLK, Os, Ot, tid);
