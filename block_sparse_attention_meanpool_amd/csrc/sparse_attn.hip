@@ -228,26 +228,25 @@ constexpr int BUFB = HALF * ROWB;        // 16 KB per half tile
 
 struct Ctx {
   __amdgpu_buffer_rsrc_t rk, rv;
-  int N, nkb, lane, w;
+  int nkb, wu;                // wu: the wave index, known uniform (readfirstlane)
+  uint32_t koff[4], voff[4];  // per-lane byte offsets of the 4 rows a lane loads
 };
 
 // Issue the asynchronous loads of half hh of key tile j into (kbuf, vbuf).
 // Each wave moves 4 KB of K and 4 KB of V: 4 instructions of 64 lanes x 16 B,
 // lane-contiguous in LDS; the global chunk each lane fetches implements the
-// swizzle.  Rows past N are clamped to N - 1 (finite data, masked in S).
+// swizzle (per-lane offsets, loop invariant).  Rows at or past N lie outside
+// the buffer's range and load as zeros (finite; their keys are masked in S).
 __device__ __forceinline__ void issue_half(const Ctx& c, int j, int hh, char* kbuf, char* vbuf) {
   const int jj = min(max(j, 0), c.nkb - 1);
+  const uint32_t tile = (uint32_t)(jj * BLK + HALF * hh) * D * 2;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int inst = 4 * c.w + e;                  // 1 KB LDS block, 4 rows
-    const int row = 4 * inst + (c.lane >> 4);      // row within the half tile
-    const int grow = min(jj * BLK + HALF * hh + row, c.N - 1);
-    const int kch = (c.lane & 15) ^ row_swz<16>(row);
-    const int vch = (c.lane & 15) ^ trs_swz(row);
+    const int inst = 4 * c.wu + e;                 // 1 KB LDS block, 4 rows
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rk, (lds_void_ptr)(kbuf + inst * 1024), 16,
-                                             (uint32_t)(grow * D + kch * 8) * 2, 0, 0, 0);
+                                             c.koff[e] + tile, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rv, (lds_void_ptr)(vbuf + inst * 1024), 16,
-                                             (uint32_t)(grow * D + vch * 8) * 2, 0, 0, 0);
+                                             c.voff[e] + tile, 0, 0, 0);
   }
 }
 
@@ -339,10 +338,14 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   Ctx c;
   c.rk = make_rsrc(k + head_off, head_bytes);
   c.rv = make_rsrc(v + head_off, head_bytes);
-  c.N = N;
   c.nkb = nkb;
-  c.lane = lane;
-  c.w = w;
+  c.wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = 4 * (4 * w + e) + (lane >> 4);  // row within the half tile
+    c.koff[e] = (uint32_t)(row * D + ((lane & 15) ^ row_swz<16>(row)) * 8) * 2;
+    c.voff[e] = (uint32_t)(row * D + ((lane & 15) ^ trs_swz(row)) * 8) * 2;
+  }
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
 
   const int count = LIST ? min(cnt[bh * nqb + qb], kmax) : nkb;
