@@ -95,9 +95,11 @@ __global__ __launch_bounds__(256) void col_lists_kernel(const uint32_t* __restri
 __device__ __forceinline__ void issue_rows(const __amdgpu_buffer_rsrc_t& ra,
                                            const __amdgpu_buffer_rsrc_t& rb, int row0, char* abuf,
                                            char* bbuf, int lane, int w) {
+  // the wave index, known uniform: the LDS destinations stay scalar
+  const int wu = __builtin_amdgcn_readfirstlane(w);
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    const int inst = 4 * w + e;
+    const int inst = 4 * wu + e;
     const int row = 4 * inst + (lane >> 4);
     const int ch = (lane & 15) ^ dual_swz(row);
     const uint32_t off = (uint32_t)((row0 + row) * D + ch * 8) * 2;
