@@ -5,6 +5,8 @@
 // state:  per key tile j, H_j = phi(K_j)^T V_j (d x d) and z_j = sum phi(K_j),
 //         one workgroup per tile; both operands are staged token-contiguous in
 //         LDS (the contraction runs over tokens) and multiplied on bf16 MFMA.
+//         At d = 128 with 128-token tiles, lin_state_pipe_kernel computes the
+//         same states with the tiles streamed through LDS-direct loads.
 //         H_j is stored transposed, bf16, as a row of the head's state matrix
 //         Ht[j][d2 * d + d1].
 // mask:   each query block's marginal list as a row of a bit matrix, and
@@ -109,6 +111,154 @@ __global__ __launch_bounds__(256) void lin_state_kernel(const uint16_t* __restri
     }
   }
 }
+
+// d = 128, 128-token tiles: the same states, streamed.  Each workgroup takes
+// two consecutive tiles of one head and reads them as four 64-token halves
+// through double-buffered LDS by LDS-direct loads (K and V rows, row-major,
+// with the transpose-read swizzle), the next half's loads in flight while the
+// current half's MFMAs run.  Transpose reads give a lane 8 consecutive tokens
+// of one feature: the layout of both MFMA operands of a product that
+// contracts over tokens.  phi is applied to the K operand in registers
+// (tokens at or past N load as zeros and give 0).  The two tiles accumulate in
+// separate registers, so the first tile's stores go out while the second
+// tile's first half is computed, and the wait before its second half (a full
+// drain, as loads and stores in flight together may complete in any order)
+// finds them done.  H_j, z_j and their summation orders are those of
+// lin_state_kernel, bit for bit.
+namespace lstate {
+
+constexpr int D = 128, BLK = 128, HALF = 64, NT = 256;
+constexpr int BUFB = HALF * D * 2;  // 16 KB: one 64-token half of K or V
+
+struct Ctx {
+  __amdgpu_buffer_rsrc_t rk, rv;
+  int wu;           // the wave index, known uniform
+  uint32_t off[4];  // per-lane byte offsets of the 4 rows a lane loads
+};
+
+__device__ __forceinline__ void issue(const Ctx& c, int tile, int hh, char* kb, char* vb) {
+  const uint32_t t = (uint32_t)(tile * BLK + HALF * hh) * D * 2;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rk, (lds_void_ptr)(kb + (4 * c.wu + e) * 1024), 16,
+                                             c.off[e] + t, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rv, (lds_void_ptr)(vb + (4 * c.wu + e) * 1024), 16,
+                                             c.off[e] + t, 0, 0, 0);
+  }
+}
+
+// phi of 8 bf16 values of tokens tok0 .. tok0 + 7 (low half of each dword
+// first); tokens at or past N give 0.
+__device__ __forceinline__ u32x4 phi8_tokens(u32x4 x, int tok0, int N) {
+  u32x4 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = tok0 + 2 * e < N ? phi(bf16_bits_to_f32(x[e] & 0xffffu)) : 0.f;
+    const float b = tok0 + 2 * e + 1 < N ? phi(bf16_bits_to_f32(x[e] >> 16)) : 0.f;
+    r[e] = pack_bf16x2(a, b);
+  }
+  return r;
+}
+
+// One 64-token half into the wave's four 32x32 blocks of H (rows d1 of block
+// w, every d2) and into z of feature 32 w + lane % 32, summed in token order
+// by the lane of the lower 32 (it takes the upper lane's 8 tokens after its own).
+__device__ __forceinline__ void half(const char* kb, const char* vb, int tok0, int N, int w,
+                                     int lane, int hf, f32x16 (&acc)[4], float& z) {
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks) {
+    const u32x4 a = phi8_tokens(tr_operand(kb, 16 * ks, 32 * w, lane), tok0 + 16 * ks + 8 * hf, N);
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      acc[u] = mfma32x32x16(a, tr_operand(vb, 16 * ks, 32 * u, lane), acc[u]);
+    // every lane gets both lanes' dwords: the lower lane's 8 tokens, then the upper lane's
+    uint32_t lo8[4], hi8[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(a[e], a[e], false, false);
+      lo8[e] = sw[0];
+      hi8[e] = sw[1];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z += bf16_bits_to_f32(lo8[e] & 0xffffu) + bf16_bits_to_f32(lo8[e] >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) z += bf16_bits_to_f32(hi8[e] & 0xffffu) + bf16_bits_to_f32(hi8[e] >> 16);
+  }
+}
+
+// H^T row of a tile (lin_state_kernel's layout) and z (lanes of the lower 32).
+__device__ __forceinline__ void store_tile(uint16_t* __restrict__ Ht, float* __restrict__ Zs,
+                                           int64_t row, const f32x16 (&acc)[4], float z, int w,
+                                           int l32, int hf) {
+  uint16_t* Hj = Ht + row * (int64_t)D * D;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int d2 = 32 * u + l32;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int d1 = 32 * w + 8 * g + 4 * hf;
+      *(u32x2*)(Hj + d2 * D + d1) = u32x2{pack_bf16x2(acc[u][4 * g], acc[u][4 * g + 1]),
+                                          pack_bf16x2(acc[u][4 * g + 2], acc[u][4 * g + 3])};
+    }
+  }
+  if (hf == 0) Zs[row * D + 32 * w + l32] = z;
+}
+
+__global__ __launch_bounds__(NT) void lin_state_pipe_kernel(const uint16_t* __restrict__ k,
+                                                            const uint16_t* __restrict__ v, int N,
+                                                            int nkb, int npairs,
+                                                            uint16_t* __restrict__ Ht,
+                                                            float* __restrict__ Zs) {
+  __shared__ __attribute__((aligned(1024))) char K0[BUFB];
+  __shared__ __attribute__((aligned(1024))) char V0[BUFB];
+  __shared__ __attribute__((aligned(1024))) char K1[BUFB];
+  __shared__ __attribute__((aligned(1024))) char V1[BUFB];
+  const int64_t bh = blockIdx.x / npairs;
+  const int t0 = 2 * (blockIdx.x % npairs);
+  const bool two = t0 + 1 < nkb;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int64_t head_off = bh * (int64_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  Ctx c;
+  c.rk = make_rsrc(k + head_off, head_bytes);
+  c.rv = make_rsrc(v + head_off, head_bytes);
+  c.wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int row = 4 * (4 * w + e) + (lane >> 4);  // row within the half
+    c.off[e] = (uint32_t)(row * D + ((lane & 15) ^ trs_swz(row)) * 8) * 2;
+  }
+  f32x16 acc0[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  f32x16 acc1[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
+  float z0 = 0.f, z1 = 0.f;
+  const int64_t row0 = bh * nkb + t0;
+
+  issue(c, t0, 0, K0, V0);
+  wait_vmcnt0();
+  __syncthreads();
+  issue(c, t0, 1, K1, V1);
+  half(K0, V0, t0 * BLK, N, w, lane, hf, acc0, z0);
+  wait_vmcnt0();
+  __syncthreads();  // every wave is done with buffer 0
+  if (two) issue(c, t0 + 1, 0, K0, V0);
+  half(K1, V1, t0 * BLK + HALF, N, w, lane, hf, acc0, z0);
+  if (two) {
+    wait_vmcnt0();
+    __syncthreads();  // every wave is done with buffer 1
+    issue(c, t0 + 1, 1, K1, V1);
+    store_tile(Ht, Zs, row0, acc0, z0, w, l32, hf);
+    half(K0, V0, (t0 + 1) * BLK, N, w, lane, hf, acc1, z1);
+    wait_vmcnt0();
+    __syncthreads();  // the first tile's stores are done too
+    half(K1, V1, (t0 + 1) * BLK + HALF, N, w, lane, hf, acc1, z1);
+    store_tile(Ht, Zs, row0 + 1, acc1, z1, w, l32, hf);
+  } else {
+    store_tile(Ht, Zs, row0, acc0, z0, w, l32, hf);
+  }
+}
+
+}  // namespace lstate
 
 // Sum of the rows src[j] (fp32, D features) over the set bits j of a bit row
 // held in LDS (W <= 128 words), strictly in ascending j: the set bits are
@@ -444,7 +594,13 @@ static hipError_t launch_linear_prepare_t(const uint16_t* k, const uint16_t* v, 
                                           int nb, const int32_t* idx, const int32_t* cnt, int kmax,
                                           void* ws, hipStream_t s) {
   const LinearPtrs lp = linear_ws_ptrs(ws, BH, nb, D);
-  lin_state_kernel<D, BLK><<<dim3((unsigned)(BH * nb)), 256, 0, s>>>(k, v, N, nb, lp.Ht, lp.Zs);
+  if constexpr (D == 128 && BLK == 128) {
+    const int npairs = (nb + 1) / 2;
+    lstate::lin_state_pipe_kernel<<<dim3((unsigned)(BH * npairs)), lstate::NT, 0, s>>>(
+        k, v, N, nb, npairs, lp.Ht, lp.Zs);
+  } else {
+    lin_state_kernel<D, BLK><<<dim3((unsigned)(BH * nb)), 256, 0, s>>>(k, v, N, nb, lp.Ht, lp.Zs);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t rows = BH * nb;
