@@ -38,6 +38,9 @@ SMALL = [
     # block holds 60 tokens, so its second 64-key half is empty
     Spec(107, "sla3_d128_b128_two_batches", B=2, H=2, N=700, d=128, block=128, kind="fourier",
          grid=(7, 10, 10), mode="sla3", keep=F(2, 6), marg=F(2, 6)),
+    # an odd number of key tiles (the linear-branch states go in pairs) with a ragged last one
+    Spec(108, "sla3_d128_b128_odd_tiles", B=1, H=2, N=1100, d=128, block=128, kind="fourier",
+         grid=(11, 10, 10), mode="sla3", keep=F(2, 9), marg=F(3, 9)),
 ]
 
 
