@@ -450,12 +450,12 @@ class SlaAttention(torch.autograd.Function):
         return dq, dk, dv, None, None, None, None, None
 
 
-def sla_attention(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=None,
-                  stream=None):
+def sla_attention(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=None):
     """Selection (no gradient) followed by SlaAttention: the differentiable
-    form of forward().  Returns (o, lists) with lists = (cls, crit_idx,
+    form of forward().  Everything runs on the current stream, as autograd's
+    own backward does.  Returns (o, lists) with lists = (cls, crit_idx,
     crit_cnt, marg_idx, marg_cnt)."""
     with torch.no_grad():
-        lists = _select(q.detach(), k.detach(), block, mode, keep, marg, thr, cls, stream)
+        lists = _select(q.detach(), k.detach(), block, mode, keep, marg, thr, cls, None)
     _, crit_idx, crit_cnt, marg_idx, marg_cnt = lists
     return SlaAttention.apply(q, k, v, block, crit_idx, crit_cnt, marg_idx, marg_cnt), lists
