@@ -81,3 +81,24 @@ def test_autograd_topk_no_linear_branch():
     say("[autograd] top-k selection (no marginal tiles), N=700")
     lists = _case(spec, 3, mode="topk", keep=spec.keep)
     assert lists[3] is None
+
+
+def test_autograd_expanded_output_gradient():
+    """o.sum() hands backward a broadcast (stride-0) gradient of ones."""
+    spec = Spec(314, "ag_sum", B=1, H=2, N=600, d=128, block=128, kind="fourier",
+                grid=(6, 10, 10), mode="sla3", keep=F(2, 5), marg=F(1, 5))
+    say("[autograd] gradient of o.sum(), N=600")
+    data = generate(spec, repairs=None, threads=1)
+    q, k, v = (_leaf(data[t]) for t in "qkv")
+    o, (cls, ci, cc, mi, mc) = sla.sla_attention(q, k, v, spec.block, mode="sla3", keep=spec.keep,
+                                                 marg=spec.marg)
+    o.sum().backward()
+    qd, kd, vd = q.detach(), k.detach(), v.detach()
+    ones = torch.ones(o.shape, dtype=torch.bfloat16, device=o.device)
+    o_s, lse = sla.sla_sparse_attn_fwd(qd, kd, vd, spec.block, ci, cc, o_fp32=True, want_lse=True)
+    dq, dk, dv = sla.sla_sparse_attn_bwd(qd, kd, vd, spec.block, ci, cc, o_s, lse, ones)
+    lin_ws = sla.sla_linear_branch_prepare(kd, vd, spec.block, mi, mc)
+    sla.sla_linear_branch_bwd(qd, kd, vd, spec.block, mi, mc, ones, lin_ws, dq, dk, dv)
+    torch.cuda.synchronize()
+    for t, want, n in ((q, dq, "dQ"), (k, dk, "dK"), (v, dv, "dV")):
+        assert torch.equal(t.grad.view(torch.int16), want.to(torch.bfloat16).view(torch.int16)), n
