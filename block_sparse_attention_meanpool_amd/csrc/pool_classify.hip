@@ -62,74 +62,85 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// Scores: S[bh][i][j] = scale * qbar_i . kbar_j in fp32, each dot product one
-// fmaf chain in feature order.  TS x TS output tile per workgroup (TS = 64 or
-// 128), 256 threads with R x R outputs each (R = TS / 16; rows R*ti..,
-// columns R*tj..), features staged through LDS in slices of 16; a thread's R
-// row and R column operands are 16-byte LDS reads.
+// Scores: S[bh][i][j] = scale * qbar_i . kbar_j in fp32 on the matrix cores
+// (v_mfma_f32_32x32x2_f32: fp32 products, fp32 sums; the feature order of the
+// sums is the instruction's, not a plain chain).  TS x TS output tile per
+// workgroup (TS = 64 or 128), four waves in a 2 x 2 arrangement, each wave
+// WB x WB blocks of 32 x 32 (WB = TS / 64).  Operands come straight from
+// global memory (the pooled tensors are small and L2-resident): in each
+// chunk of 8 features, lane half h holds features 4h + 0..3 of its row
+// (16 bytes), and MFMA step u pairs feature u (half 0) with 4 + u (half 1);
+// Q and K use the same pairing, so every feature enters each dot product once.
+// Rows past nb load as zeros (buffer range) and are not stored.
 // ---------------------------------------------------------------------------
 template <int D, int TS>
 __global__ __launch_bounds__(256) void score_kernel(const float* __restrict__ qp,
                                                     const float* __restrict__ kp,
                                                     float* __restrict__ S, int nb, float scale) {
-  constexpr int KS = 16, R = TS / 16, LD = TS / 64;
-  __shared__ __attribute__((aligned(16))) float qs[KS][TS];
-  __shared__ __attribute__((aligned(16))) float ks[KS][TS];
+  constexpr int WB = TS / 64, CH = D / 8;
   const int64_t bh = blockIdx.z;
-  const int i0 = blockIdx.y * TS, j0 = blockIdx.x * TS;
-  const float* qh = qp + bh * nb * D;
-  const float* kh = kp + bh * nb * D;
-  const int t = threadIdx.x;
-  const int ti = t / 16, tj = t % 16;
-  float acc[R][R] = {};
-  for (int f0 = 0; f0 < D; f0 += KS) {
-    // TS rows x 16 features per operand, read as 4 consecutive features of
-    // one row (16 bytes), LD reads per thread and operand.
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int i0 = blockIdx.y * TS + (w >> 1) * (TS / 2);
+  const int j0 = blockIdx.x * TS + (w & 1) * (TS / 2);
+  const uint32_t head_bytes = (uint32_t)nb * D * 4;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(qp + bh * nb * D, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(kp + bh * nb * D, head_bytes);
+  uint32_t qoff[WB], koff[WB];
 #pragma unroll
-    for (int e = 0; e < LD; ++e) {
-      const int idx = t + 256 * e;  // row idx / 4, features 4 * (idx % 4)
-      const int row = idx / 4, f = 4 * (idx % 4);
-      const int gi = i0 + row, gj = j0 + row;
-      const f32x4 a = gi < nb ? *(const f32x4*)(qh + (int64_t)gi * D + f0 + f) : f32x4{};
-      const f32x4 b = gj < nb ? *(const f32x4*)(kh + (int64_t)gj * D + f0 + f) : f32x4{};
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        qs[f + u][row] = a[u];
-        ks[f + u][row] = b[u];
-      }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int f = 0; f < KS; ++f) {
-      float a[R], b[R];
-#pragma unroll
-      for (int v = 0; v < R / 4; ++v) {
-        const f32x4 av = *(const f32x4*)&qs[f][R * ti + 4 * v];
-        const f32x4 bv = *(const f32x4*)&ks[f][R * tj + 4 * v];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          a[4 * v + u] = av[u];
-          b[4 * v + u] = bv[u];
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < R; ++u)
-#pragma unroll
-        for (int w = 0; w < R; ++w) acc[u][w] = fmaf(a[u], b[w], acc[u][w]);
-    }
-    __syncthreads();
+  for (int b = 0; b < WB; ++b) {
+    qoff[b] = (uint32_t)((i0 + 32 * b + l32) * D + 4 * hf) * 4;
+    koff[b] = (uint32_t)((j0 + 32 * b + l32) * D + 4 * hf) * 4;
   }
+  f32x16 acc[WB][WB];
+#pragma unroll
+  for (int a = 0; a < WB; ++a)
+#pragma unroll
+    for (int b = 0; b < WB; ++b) acc[a][b] = f32x16{};
+  f32x4 qa[WB], kb[WB];
+#pragma unroll
+  for (int b = 0; b < WB; ++b) {
+    qa[b] = __builtin_bit_cast(f32x4, buf_load16(rq, qoff[b]));
+    kb[b] = __builtin_bit_cast(f32x4, buf_load16(rk, koff[b]));
+  }
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    f32x4 qn[WB], kn[WB];
+    if (c + 1 < CH) {
+#pragma unroll
+      for (int b = 0; b < WB; ++b) {
+        qn[b] = __builtin_bit_cast(f32x4, buf_load16(rq, qoff[b] + 32 * (c + 1)));
+        kn[b] = __builtin_bit_cast(f32x4, buf_load16(rk, koff[b] + 32 * (c + 1)));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int a = 0; a < WB; ++a)
+#pragma unroll
+        for (int b = 0; b < WB; ++b)
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[a][u], kb[b][u], acc[a][b], 0, 0, 0);
+    if (c + 1 < CH) {
+#pragma unroll
+      for (int b = 0; b < WB; ++b) {
+        qa[b] = qn[b];
+        kb[b] = kn[b];
+      }
+    }
+  }
+  // C layout: register r of a lane holds row 8 (r / 4) + 4 hf + r % 4, column l32
   float* Sh = S + bh * (int64_t)nb * nb;
 #pragma unroll
-  for (int u = 0; u < R; ++u) {
-    const int gi = i0 + R * ti + u;
-    if (gi >= nb) continue;
+  for (int a = 0; a < WB; ++a)
 #pragma unroll
-    for (int w = 0; w < R; ++w) {
-      const int gj = j0 + R * tj + w;
-      if (gj < nb) Sh[(int64_t)gi * nb + gj] = scale * acc[u][w];
+    for (int b = 0; b < WB; ++b) {
+      const int gj = j0 + 32 * b + l32;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int gi = i0 + 32 * a + 8 * (r / 4) + 4 * hf + r % 4;
+        if (gi < nb && gj < nb) Sh[(int64_t)gi * nb + gj] = scale * acc[a][b][r];
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------
