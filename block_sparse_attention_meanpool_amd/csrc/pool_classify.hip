@@ -159,11 +159,6 @@ __device__ __forceinline__ uint64_t order_key(float s, int j) {
   return ((uint64_t)u << 12) | (uint64_t)(4095 - j);
 }
 
-__device__ __forceinline__ int wave_sum_i(int x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
 __device__ __forceinline__ float wave_sum_f(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
@@ -179,15 +174,19 @@ __device__ __forceinline__ float wave_max_f(float x) {
 // top while at least k keys stay above the candidate; once exactly k do, the
 // candidate already separates the k largest from the rest (the same set the
 // k-th largest key itself would select), so the remaining bits are skipped.
+// The k-th largest key of a row spread over a wave (slot t of lane l holds
+// entry l + 64 t; absent entries hold key 0, below every candidate).  The
+// count of keys at or above a candidate is one compare per slot, its ballot
+// counted on the scalar unit; slots past the row (t >= nt) are skipped.
 template <int MC>
-__device__ __forceinline__ uint64_t kth_largest(const uint64_t (&key)[MC], int n_here, int k) {
+__device__ __forceinline__ uint64_t kth_largest(const uint64_t (&key)[MC], int nt, int k) {
   uint64_t T = 0;
   for (int bit = 43; bit >= 0; --bit) {
     const uint64_t cand = T | (1ull << bit);
     int c = 0;
 #pragma unroll
-    for (int t = 0; t < MC; ++t) c += (t < n_here && key[t] >= cand) ? 1 : 0;
-    c = wave_sum_i(c);
+    for (int t = 0; t < MC; ++t)
+      if (t < nt) c += __popcll(__builtin_amdgcn_ballot_w64(key[t] >= cand));
     if (c >= k) {
       T = cand;
       if (c == k) break;
@@ -245,8 +244,9 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
     }
     t_crit = T;
   } else {
-    t_crit = kth_largest<MC>(key, n_here, kc);
-    if (mode == 2 && km > 0) t_marg = kth_largest<MC>(key, n_here, kc + km);
+    const int nt = (nb + 63) / 64;
+    t_crit = kth_largest<MC>(key, nt, kc);
+    if (mode == 2 && km > 0) t_marg = kth_largest<MC>(key, nt, kc + km);
   }
 #pragma unroll
   for (int t = 0; t < MC; ++t) {
