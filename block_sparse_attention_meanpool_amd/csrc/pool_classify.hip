@@ -177,16 +177,22 @@ __device__ __forceinline__ float wave_max_f(float x) {
 // The k-th largest key of a row spread over a wave (slot t of lane l holds
 // entry l + 64 t; absent entries hold key 0, below every candidate).  The
 // count of keys at or above a candidate is one compare per slot, its ballot
-// counted on the scalar unit; slots past the row (t >= nt) are skipped.
+// counted on the scalar unit.  Every slot is compared (no branch per slot),
+// so the compares issue back to back; the launch picks MC close to nb / 64.
 template <int MC>
-__device__ __forceinline__ uint64_t kth_largest(const uint64_t (&key)[MC], int nt, int k) {
+__device__ __forceinline__ uint64_t kth_largest(const uint64_t (&key)[MC], int k) {
   uint64_t T = 0;
   for (int bit = 43; bit >= 0; --bit) {
     const uint64_t cand = T | (1ull << bit);
     int c = 0;
 #pragma unroll
-    for (int t = 0; t < MC; ++t)
-      if (t < nt) c += __popcll(__builtin_amdgcn_ballot_w64(key[t] >= cand));
+    for (int g = 0; g < MC; g += 4) {  // four ballots live at once: no wait between compares
+      uint64_t b[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) b[t] = __builtin_amdgcn_ballot_w64(key[g + t] >= cand);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) c += __popcll(b[t]);
+    }
     if (c >= k) {
       T = cand;
       if (c == k) break;
@@ -244,9 +250,8 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ S
     }
     t_crit = T;
   } else {
-    const int nt = (nb + 63) / 64;
-    t_crit = kth_largest<MC>(key, nt, kc);
-    if (mode == 2 && km > 0) t_marg = kth_largest<MC>(key, nt, kc + km);
+    t_crit = kth_largest<MC>(key, kc);
+    if (mode == 2 && km > 0) t_marg = kth_largest<MC>(key, kc + km);
   }
 #pragma unroll
   for (int t = 0; t < MC; ++t) {
@@ -289,10 +294,14 @@ hipError_t launch_scores(const float* qp, const float* kp, float* S, int64_t BH,
 hipError_t launch_select(const float* S, uint8_t* cls, int64_t rows, int nb, int mode, int kc,
                          int km, float thr, hipStream_t s) {
   dim3 grid((unsigned)((rows + 3) / 4));
+  // MC = slots per lane: the smallest of these that holds nb keys
   if (nb <= 256) select_kernel<4><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
   else if (nb <= 512) select_kernel<8><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
+  else if (nb <= 768) select_kernel<12><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
   else if (nb <= 1024) select_kernel<16><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
+  else if (nb <= 1536) select_kernel<24><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
   else if (nb <= 2048) select_kernel<32><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
+  else if (nb <= 3072) select_kernel<48><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
   else select_kernel<64><<<grid, 256, 0, s>>>(S, cls, rows, nb, mode, kc, km, thr);
   return hipGetLastError();
 }
