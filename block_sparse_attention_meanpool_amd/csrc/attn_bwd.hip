@@ -299,31 +299,6 @@ __device__ __forceinline__ void sdp_block(const char* qbuf, const char* obuf, co
   }
 }
 
-// P = exp2(S sl2 - LSE log2 e) and dS = P (dP - D), as bf16 B operands; register r
-// of the accumulators holds query 32 qb2 + 16 (r / 8) + 8 hf + r % 8 of the half.
-__device__ __forceinline__ void pds_block(const float* lbuf, const float* ebuf, int qb2, int hf,
-                                          float sl2, const f32x16& sacc, const f32x16& dpacc,
-                                          u32x4 (&pb)[2], u32x4 (&dsb)[2]) {
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs) {
-    const int q0 = 32 * qb2 + 16 * hs + 8 * hf;
-    const f32x4 la = *(const f32x4*)(lbuf + q0), lb = *(const f32x4*)(lbuf + q0 + 4);
-    const f32x4 ea = *(const f32x4*)(ebuf + q0), eb = *(const f32x4*)(ebuf + q0 + 4);
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int r = 8 * hs + 2 * p;
-      const float l0 = p < 2 ? la[2 * p] : lb[2 * p - 4];
-      const float l1 = p < 2 ? la[2 * p + 1] : lb[2 * p - 3];
-      const float e0 = p < 2 ? ea[2 * p] : eb[2 * p - 4];
-      const float e1 = p < 2 ? ea[2 * p + 1] : eb[2 * p - 3];
-      const float p0 = fast_exp2(fmaf(sacc[r], sl2, -l0 * kLog2e));
-      const float p1 = fast_exp2(fmaf(sacc[r + 1], sl2, -l1 * kLog2e));
-      pb[hs][p] = pack_bf16x2(p0, p1);
-      dsb[hs][p] = pack_bf16x2(p0 * (dpacc[r] - e0), p1 * (dpacc[r + 1] - e1));
-    }
-  }
-}
-
 // dV += P^T dO and dK += dS^T Q over the sub-block's 32 queries.
 __device__ __forceinline__ void acc_block(const char* qbuf, const char* obuf, int qb2, int lane,
                                           const u32x4 (&pb)[2], const u32x4 (&dsb)[2],
@@ -339,24 +314,49 @@ __device__ __forceinline__ void acc_block(const char* qbuf, const char* obuf, in
   }
 }
 
-// One 64-query half: two sub-blocks, software-pipelined so that each
-// sub-block's softmax VALU work sits between MFMAs it does not feed (the
-// other sub-block's S/dP, then the first's dV/dK); the accumulation order of
-// dK and dV is the plain one (sub-block 0, then 1).
+// One softmax step: P = exp2(S sl2 - LSE log2 e) and dS = P (dP - D) for the
+// register pair r = 8 hs + 2 p (queries 32 qb2 + 16 hs + 8 hf + 2 p and the
+// next), packed into the bf16 B operands pb[hs] and dsb[hs].
+__device__ __forceinline__ void pds_step(const float* lbuf, const float* ebuf, int qb2, int hf,
+                                         float sl2, const f32x16& sacc, const f32x16& dpacc,
+                                         int hs, int p, u32x4 (&pb)[2], u32x4 (&dsb)[2]) {
+  const int q0 = 32 * qb2 + 16 * hs + 8 * hf + 2 * p;
+  const f32x2 lp = *(const f32x2*)(lbuf + q0), ep = *(const f32x2*)(ebuf + q0);
+  const float l0 = lp[0], l1 = lp[1], e0 = ep[0], e1 = ep[1];
+  const int r = 8 * hs + 2 * p;
+  const float p0 = fast_exp2(fmaf(sacc[r], sl2, -l0 * kLog2e));
+  const float p1 = fast_exp2(fmaf(sacc[r + 1], sl2, -l1 * kLog2e));
+  pb[hs][p] = pack_bf16x2(p0, p1);
+  dsb[hs][p] = pack_bf16x2(p0 * (dpacc[r] - e0), p1 * (dpacc[r + 1] - e1));
+}
+
+// One 64-query half: two sub-blocks, software-pipelined by hand: each of the
+// second sub-block's eight S/dP steps (two MFMAs) carries one softmax step of
+// the first, and each of the first sub-block's eight dV/dK steps carries one
+// of the second.  dK and dV accumulate in the plain order.
 __device__ __forceinline__ void dkdv_half(const char* qbuf, const char* obuf, const float* lbuf,
                                           const float* ebuf, const u32x4 (&kf)[8],
                                           const u32x4 (&vf)[8], f32x16 (&dkacc)[4],
                                           f32x16 (&dvacc)[4], float sl2, int hf, int qrowp,
                                           int lane) {
-  f32x16 s0, d0, s1, d1;
+  f32x16 s0, d0, s1 = f32x16{}, d1 = f32x16{};
   u32x4 p0[2], ds0[2], p1[2], ds1[2];
   sdp_block(qbuf, obuf, kf, vf, 0, hf, qrowp, s0, d0);
-  sdp_block(qbuf, obuf, kf, vf, 1, hf, qrowp, s1, d1);
-  pds_block(lbuf, ebuf, 0, hf, sl2, s0, d0, p0, ds0);
-  __builtin_amdgcn_iglp_opt(2);
-  acc_block(qbuf, obuf, 0, lane, p0, ds0, dkacc, dvacc);
-  pds_block(lbuf, ebuf, 1, hf, sl2, s1, d1, p1, ds1);
-  __builtin_amdgcn_iglp_opt(2);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    s1 = mfma32x32x16(dual_row_read(qbuf, 32 + qrowp, 2 * ks + hf), kf[ks], s1);
+    d1 = mfma32x32x16(dual_row_read(obuf, 32 + qrowp, 2 * ks + hf), vf[ks], d1);
+    pds_step(lbuf, ebuf, 0, hf, sl2, s0, d0, ks >> 2, ks & 3, p0, ds0);
+  }
+#pragma unroll
+  for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int k0 = 16 * hs;
+      dvacc[db] = mfma32x32x16(tr_operand<DualSwz>(obuf, k0, 32 * db, lane), p0[hs], dvacc[db]);
+      dkacc[db] = mfma32x32x16(tr_operand<DualSwz>(qbuf, k0, 32 * db, lane), ds0[hs], dkacc[db]);
+      pds_step(lbuf, ebuf, 1, hf, sl2, s1, d1, hs, db, p1, ds1);
+    }
   acc_block(qbuf, obuf, 1, lane, p1, ds1, dkacc, dvacc);
 }
 
