@@ -441,6 +441,9 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   for (int cb = 0; cb < 4; ++cb) acc[cb][0] = acc[cb][1] = f32x16{};
   const int nchunk = (nkb + CHUNK - 1) / CHUNK;
   auto compute = [&](const char* buf, const u32x2 (&m)[2]) {
+    // a wave whose 64 query blocks mark none of the chunk's 64 key tiles adds
+    // only exact zeros: skip its MFMAs (wave-uniform; the loads are unaffected)
+    if (__ballot((m[0][0] | m[0][1] | m[1][0] | m[1][1]) != 0u) == 0) return;
 #pragma unroll
     for (int ks2 = 0; ks2 < 4; ++ks2) {
       const int sh = 16 * ks2 + 8 * hf;
