@@ -8,7 +8,8 @@
   inputs built so that every row's pooled scores are strictly ordered by key
   block with gaps far above fp32 error (a ramp spread over two features, whose
   block means take exactly representable values); masks bit-exact, sampled
-  outputs within the bars.
+  outputs within the bars; and the selection at block counts that run each
+  slot count of the top-k search.
 """
 
 import math
@@ -135,3 +136,21 @@ def test_largest_block_count():
     got = np.concatenate([o[0, 0, i * 128:(i + 1) * 128].cpu().numpy() for (_, _, i) in rows])
     want = np.concatenate([res[r][0] for r in rows])
     check_close(got, want, "O (sampled rows), nb = 4096")
+
+
+@pytest.mark.parametrize("nb", [700, 1100, 1600, 2500])
+def test_selection_slot_counts(nb):
+    """The top-k search holds a row in 4 ... 64 key slots per lane, chosen by nb:
+    these block counts run the 12, 24, 32 and 48 slot kernels.  Ramp inputs
+    (strictly ordered scores, gaps far above fp32 error); top-k and the
+    three-way split, class maps bit-exact."""
+    say(f"[edge] selection with nb = {nb} key blocks")
+    qb, kb, _ = _ramp_inputs(nb, seed=nb)
+    q64, k64 = osla.bf16_to_f64(qb), osla.bf16_to_f64(kb)
+    q, k = to_dev(qb), to_dev(kb)
+    for mode, keep, marg in (("topk", F(1, 20), None), ("sla3", F(1, 20), F(1, 10))):
+        cls_ref = osla.class_map(q64, k64, 128, mode, keep, marg)[0]
+        kc, km = osla.selection_counts(mode, nb, keep, marg)
+        cls = sla.sla_pool_classify(q, k, 128, mode, kc, km)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(cls.cpu().numpy(), cls_ref, err_msg=f"{mode}, nb = {nb}")
