@@ -33,6 +33,14 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, bf16x2));
 }
 
+// The low halves of a hi + lo bf16 split of two floats: x - bf16_rne(x) for
+// each, rounded to bf16 again (packed like pack_bf16x2).  hi + lo carries
+// about 16 significant bits of x.
+__device__ __forceinline__ uint32_t pack_bf16x2_lo(float lo, float hi) {
+  const uint32_t h = pack_bf16x2(lo, hi);
+  return pack_bf16x2(lo - __uint_as_float(h << 16), hi - __uint_as_float(h & 0xffff0000u));
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end return 0
 // and stores past the end are dropped by the hardware.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -47,6 +47,15 @@ hipError_t launch_linear_prepare(const uint16_t* k, const uint16_t* v, int64_t B
 // per head: the masked-GEMM gather (nb bit rows of W words, nb source rows)
 hipError_t launch_gather(const uint16_t* Ht, const uint32_t* bits, int64_t BH, int nb, int W, int d,
                          uint16_t* C, hipStream_t s);
+// The same product with the states as a hi + lo bf16 pair (Ht, Ht_lo), both
+// parts accumulated in fp32, the result stored as a hi + lo pair (C, C_lo)
+hipError_t launch_gather_hilo(const uint16_t* Ht, const uint16_t* Ht_lo, const uint32_t* bits,
+                              int64_t BH, int nb, int W, int d, uint16_t* C, uint16_t* C_lo,
+                              hipStream_t s);
+// The low parts H_j - bf16(H_j) of the per-tile states that
+// launch_linear_prepare stores rounded (same layout as its Ht)
+hipError_t launch_linear_states_lo(const uint16_t* k, const uint16_t* v, int64_t BH, int N, int d,
+                                   int block, int nb, uint16_t* Ht_lo, hipStream_t s);
 // out[row] = sum of src rows (fp32 [nsrc, d] per head) over the set bits of
 // bit row `row`, in ascending order; per_head bit rows per head
 hipError_t launch_bitrow_sums(const uint32_t* bits, int W, int64_t rows, int per_head, int nsrc,
@@ -82,10 +91,12 @@ hipError_t launch_attn_bwd_generic(const uint16_t* q, const uint16_t* k, const u
                                    float* Dbuf, const uint16_t* col_idx, const int32_t* col_cnt,
                                    hipStream_t s);
 // Linear-branch backward workspace: dS_i (bf16, laid out like the states),
-// dzeta_i (fp32), the transposed marginal bit matrix, dH_j (bf16), dz_j (fp32).
+// dzeta_i (fp32), the transposed marginal bit matrix, dH_j (bf16), dz_j (fp32),
+// then three arrays laid out like the states (lo_bytes each): the states' low
+// parts and S_i as a hi + lo pair.
 struct LinearBwdWs {
   int words;
-  size_t ds_bytes, dzeta_bytes, bits_bytes, dh_bytes, dz_bytes, total;
+  size_t ds_bytes, dzeta_bytes, bits_bytes, dh_bytes, dz_bytes, lo_bytes, total;
 };
 LinearBwdWs linear_bwd_ws_layout(int64_t BH, int nb, int d);
 // d in {64, 128}, block in {64, 128}; lin_ws prepared by launch_linear_prepare
@@ -98,8 +109,8 @@ hipError_t launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_
 // shapes other than d = 128 with 128-token blocks
 hipError_t launch_linear_bwd_query_generic(const uint16_t* q, const uint16_t* d_o, int64_t BH,
                                            int N, int d, int block, int nb, const uint16_t* C,
-                                           const float* zeta, float* dq, uint16_t* dS,
-                                           float* dzeta, hipStream_t s);
+                                           const uint16_t* C_lo, const float* zeta, float* dq,
+                                           uint16_t* dS, float* dzeta, hipStream_t s);
 hipError_t launch_linear_bwd_key_generic(const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                                          int d, int block, int nb, const uint16_t* dH,
                                          const float* dz, float* dk, float* dv, hipStream_t s);

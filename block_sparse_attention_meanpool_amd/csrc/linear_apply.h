@@ -28,13 +28,16 @@ __device__ __forceinline__ u32x4 phi8(u32x4 x, bool valid) {
 //   lacc  out, in the layout of the softmax branch's O^T accumulators:
 //         register r of block db holds feature 32 db + 8 (r / 4) + 4 hf + r % 4
 //         of query l32
+//   St_lo with HILO: the low bf16 part of S_i^T (same layout), multiplied
+//         into the same accumulators, so S_i enters with about 16 bits
 // Returns 1 / (phi(q) . zeta_i), or 0 when that dot product is not positive
 // (a query block with no marginal tile has S_i = 0 and zeta_i = 0).
-template <int D>
+template <int D, bool HILO = false>
 __device__ __forceinline__ float linear_apply(const uint16_t* __restrict__ St,
                                               const float* __restrict__ zt,
                                               const u32x4 (&qf)[D / 16], int l32, int hf,
-                                              f32x16 (&lacc)[D / 32]) {
+                                              f32x16 (&lacc)[D / 32],
+                                              const uint16_t* __restrict__ St_lo = nullptr) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) lacc[db] = f32x16{};
   float den = 0.f;
@@ -54,6 +57,10 @@ __device__ __forceinline__ float linear_apply(const uint16_t* __restrict__ St,
     for (int db = 0; db < D / 32; ++db) {
       const u32x4 a = *(const u32x4*)(St + (32 * db + l32) * D + 16 * ks + 8 * hf);
       lacc[db] = mfma32x32x16(a, pq, lacc[db]);
+      if constexpr (HILO) {
+        const u32x4 al = *(const u32x4*)(St_lo + (32 * db + l32) * D + 16 * ks + 8 * hf);
+        lacc[db] = mfma32x32x16(al, pq, lacc[db]);
+      }
     }
   }
   den = sum_halves(den);

@@ -25,7 +25,9 @@
 
 namespace sla {
 
-template <int D, int BLK>
+// LO: store the low part H_j - bf16(H_j) of each state instead (a hi + lo
+// pair with the states above; z_j is not written).
+template <int D, int BLK, bool LO = false>
 __global__ __launch_bounds__(256) void lin_state_kernel(const uint16_t* __restrict__ k,
                                                         const uint16_t* __restrict__ v, int N,
                                                         int nkb, uint16_t* __restrict__ Ht,
@@ -68,7 +70,7 @@ __global__ __launch_bounds__(256) void lin_state_kernel(const uint16_t* __restri
   __syncthreads();
 
   // z_j: row sums of phi(K)^T (the same bf16 values the product uses).
-  if (tid < D) {
+  if (!LO && tid < D) {
     float z = 0.f;
 #pragma unroll
     for (int c = 0; c < BLK / 8; ++c) {
@@ -106,8 +108,12 @@ __global__ __launch_bounds__(256) void lin_state_kernel(const uint16_t* __restri
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d1 = 32 * db1 + 8 * g + 4 * hf;
-      *(u32x2*)(Hj + d2 * D + d1) = u32x2{pack_bf16x2(acc[u][4 * g], acc[u][4 * g + 1]),
-                                          pack_bf16x2(acc[u][4 * g + 2], acc[u][4 * g + 3])};
+      if (LO)
+        *(u32x2*)(Hj + d2 * D + d1) = u32x2{pack_bf16x2_lo(acc[u][4 * g], acc[u][4 * g + 1]),
+                                            pack_bf16x2_lo(acc[u][4 * g + 2], acc[u][4 * g + 3])};
+      else
+        *(u32x2*)(Hj + d2 * D + d1) = u32x2{pack_bf16x2(acc[u][4 * g], acc[u][4 * g + 1]),
+                                            pack_bf16x2(acc[u][4 * g + 2], acc[u][4 * g + 3])};
     }
   }
 }
@@ -186,7 +192,9 @@ __device__ __forceinline__ void half(const char* kb, const char* vb, int tok0, i
   }
 }
 
-// H^T row of a tile (lin_state_kernel's layout) and z (lanes of the lower 32).
+// H^T row of a tile (lin_state_kernel's layout) and z (lanes of the lower 32);
+// with LO the low parts H - bf16(H) and no z.
+template <bool LO>
 __device__ __forceinline__ void store_tile(uint16_t* __restrict__ Ht, float* __restrict__ Zs,
                                            int64_t row, const f32x16 (&acc)[4], float z, int w,
                                            int l32, int hf) {
@@ -197,13 +205,18 @@ __device__ __forceinline__ void store_tile(uint16_t* __restrict__ Ht, float* __r
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int d1 = 32 * w + 8 * g + 4 * hf;
-      *(u32x2*)(Hj + d2 * D + d1) = u32x2{pack_bf16x2(acc[u][4 * g], acc[u][4 * g + 1]),
-                                          pack_bf16x2(acc[u][4 * g + 2], acc[u][4 * g + 3])};
+      if (LO)
+        *(u32x2*)(Hj + d2 * D + d1) = u32x2{pack_bf16x2_lo(acc[u][4 * g], acc[u][4 * g + 1]),
+                                            pack_bf16x2_lo(acc[u][4 * g + 2], acc[u][4 * g + 3])};
+      else
+        *(u32x2*)(Hj + d2 * D + d1) = u32x2{pack_bf16x2(acc[u][4 * g], acc[u][4 * g + 1]),
+                                            pack_bf16x2(acc[u][4 * g + 2], acc[u][4 * g + 3])};
     }
   }
-  if (hf == 0) Zs[row * D + 32 * w + l32] = z;
+  if (!LO && hf == 0) Zs[row * D + 32 * w + l32] = z;
 }
 
+template <bool LO>
 __global__ __launch_bounds__(NT) void lin_state_pipe_kernel(const uint16_t* __restrict__ k,
                                                             const uint16_t* __restrict__ v, int N,
                                                             int nkb, int npairs,
@@ -247,14 +260,14 @@ __global__ __launch_bounds__(NT) void lin_state_pipe_kernel(const uint16_t* __re
     wait_vmcnt0();
     __syncthreads();  // every wave is done with buffer 1
     issue(c, t0 + 1, 1, K1, V1);
-    store_tile(Ht, Zs, row0, acc0, z0, w, l32, hf);
+    store_tile<LO>(Ht, Zs, row0, acc0, z0, w, l32, hf);
     half(K0, V0, (t0 + 1) * BLK, N, w, lane, hf, acc1, z1);
     wait_vmcnt0();
     __syncthreads();  // the first tile's stores are done too
     half(K1, V1, (t0 + 1) * BLK + HALF, N, w, lane, hf, acc1, z1);
-    store_tile(Ht, Zs, row0 + 1, acc1, z1, w, l32, hf);
+    store_tile<LO>(Ht, Zs, row0 + 1, acc1, z1, w, l32, hf);
   } else {
-    store_tile(Ht, Zs, row0, acc0, z0, w, l32, hf);
+    store_tile<LO>(Ht, Zs, row0, acc0, z0, w, l32, hf);
   }
 }
 
@@ -378,15 +391,23 @@ __device__ __forceinline__ u32x4 bits_to_bf16(uint32_t b8) {
 // row tile, so taller row tiles cut the Ht traffic.  Each lane's mask words
 // for the next chunk are loaded into registers while the current one is
 // multiplied, and become the bf16 1.0 / 0.0 operand.
-template <int D, int WAVES>
+// HILO: the states come as a hi + lo bf16 pair (Ht, Ht_lo); both parts are
+// multiplied into the same fp32 accumulators (the 0/1 operand is exact), and
+// the sum is stored as a hi + lo pair too (C, C_lo): S_i to about 16
+// significant bits, for the backward's cancelling dQ terms.
+template <int D, int WAVES, bool HILO>
 __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void lin_gather_kernel(
-    const uint16_t* __restrict__ Ht, const uint32_t* __restrict__ bits, int nqb, int nkb, int W,
-    int rowtiles, int coltiles, int per_xcd, int64_t tiles, uint16_t* __restrict__ C) {
+    const uint16_t* __restrict__ Ht, const uint16_t* __restrict__ Ht_lo,
+    const uint32_t* __restrict__ bits, int nqb, int nkb, int W, int rowtiles, int coltiles,
+    int per_xcd, int64_t tiles, uint16_t* __restrict__ C, uint16_t* __restrict__ C_lo) {
   constexpr int DD = D * D;
   constexpr int CHUNK = 64, COLS = 128, BUFB = CHUNK * COLS * 2;  // 16 KB
   constexpr int ROWS = 64 * WAVES, NI = (16 + WAVES - 1) / WAVES;  // 1 KB DMA blocks per wave
+  constexpr int LOB = HILO ? BUFB : 1024;
   __shared__ __attribute__((aligned(1024))) char B0[BUFB];
   __shared__ __attribute__((aligned(1024))) char B1[BUFB];
+  __shared__ __attribute__((aligned(1024))) char L0[LOB];
+  __shared__ __attribute__((aligned(1024))) char L1[LOB];
 
   // XCD-aware order: logical tiles [x * per_xcd, (x+1) * per_xcd) run on XCD x,
   // row tiles fastest, so the row tiles sharing one column slice of Ht meet in
@@ -402,6 +423,8 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const __amdgpu_buffer_rsrc_t rh = make_rsrc(Ht + bh * (int64_t)nkb * DD, (uint32_t)nkb * DD * 2);
+  const __amdgpu_buffer_rsrc_t rl =
+      make_rsrc((HILO ? Ht_lo : Ht) + bh * (int64_t)nkb * DD, (uint32_t)nkb * DD * 2);
   const int wu = __builtin_amdgcn_readfirstlane(w);
   uint32_t voff[8];  // NI <= 8 entries used; a size that depends on WAVES, captured by the
                      // lambda below, makes the host compiler drop the kernel's launch stub
@@ -411,13 +434,17 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
     voff[e] = (uint32_t)(row * DD + ((lane & 15) ^ trs_swz(row)) * 8) * 2;
   }
   // Rows past nkb fall outside the buffer range and land in LDS as zeros.
-  auto issue = [&](int chunk, char* buf) {
+  auto issue = [&](int chunk, char* buf, char* lbuf) {
     const int soff = (chunk * CHUNK * DD + c0) * 2;
 #pragma unroll
     for (int e = 0; e < NI; ++e)
-      if (wu + WAVES * e < 16)
+      if (wu + WAVES * e < 16) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lds_void_ptr)(buf + (wu + WAVES * e) * 1024),
                                                  16, voff[e], soff, 0, 0);
+        if (HILO)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void_ptr)(lbuf + (wu + WAVES * e) * 1024),
+                                                   16, voff[e], soff, 0, 0);
+      }
   };
 
   // this lane's two query blocks (one per MFMA row group); rows past nqb get no bits
@@ -440,7 +467,7 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
   for (int cb = 0; cb < 4; ++cb) acc[cb][0] = acc[cb][1] = f32x16{};
   const int nchunk = (nkb + CHUNK - 1) / CHUNK;
-  auto compute = [&](const char* buf, const u32x2 (&m)[2]) {
+  auto compute = [&](const char* buf, const char* lbuf, const u32x2 (&m)[2]) {
     // a wave whose 64 query blocks mark none of the chunk's 64 key tiles adds
     // only exact zeros: skip its MFMAs (wave-uniform; the loads are unaffected)
     if (__ballot((m[0][0] | m[0][1] | m[1][0] | m[1][1]) != 0u) == 0) return;
@@ -456,30 +483,35 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
         const u32x4 a = tr_operand(buf, 16 * ks2, 32 * cb, lane);
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) acc[cb][rb] = mfma32x32x16(a, b[rb], acc[cb][rb]);
+        if (HILO) {
+          const u32x4 al = tr_operand(lbuf, 16 * ks2, 32 * cb, lane);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) acc[cb][rb] = mfma32x32x16(al, b[rb], acc[cb][rb]);
+        }
       }
     }
   };
 
-  issue(0, B0);
+  issue(0, B0, L0);
   load_bits(0);
   for (int ch = 0; ch < nchunk; ch += 2) {
     wait_vmcnt0();
     __syncthreads();  // B0 and mb hold chunk ch; every wave is done with B1
     const u32x2 m0[2] = {mb[0], mb[1]};
     if (ch + 1 < nchunk) {
-      issue(ch + 1, B1);
+      issue(ch + 1, B1, L1);
       load_bits(ch + 1);
     }
-    compute(B0, m0);
+    compute(B0, L0, m0);
     if (ch + 1 < nchunk) {
       wait_vmcnt0();
       __syncthreads();  // B1 and mb hold chunk ch + 1; every wave is done with B0
       const u32x2 m1[2] = {mb[0], mb[1]};
       if (ch + 2 < nchunk) {
-        issue(ch + 2, B0);
+        issue(ch + 2, B0, L0);
         load_bits(ch + 2);
       }
-      compute(B1, m1);
+      compute(B1, L1, m1);
     }
   }
 
@@ -488,14 +520,19 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(2, 2
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     if (!mok[rb]) continue;
-    uint16_t* crow = C + ((int64_t)bh * nqb + i0 + 64 * w + 32 * rb + l32) * DD + c0;
+    const int64_t roff = ((int64_t)bh * nqb + i0 + 64 * w + 32 * rb + l32) * DD + c0;
+    uint16_t* crow = C + roff;
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int col = 32 * cb + 8 * g + 4 * hf;
-        *(u32x2*)(crow + col) = u32x2{pack_bf16x2(acc[cb][rb][4 * g], acc[cb][rb][4 * g + 1]),
-                                      pack_bf16x2(acc[cb][rb][4 * g + 2], acc[cb][rb][4 * g + 3])};
+        const f32x16& a = acc[cb][rb];
+        *(u32x2*)(crow + col) = u32x2{pack_bf16x2(a[4 * g], a[4 * g + 1]),
+                                      pack_bf16x2(a[4 * g + 2], a[4 * g + 3])};
+        if (HILO)
+          *(u32x2*)(C_lo + roff + col) = u32x2{pack_bf16x2_lo(a[4 * g], a[4 * g + 1]),
+                                               pack_bf16x2_lo(a[4 * g + 2], a[4 * g + 3])};
       }
   }
 }
@@ -599,7 +636,7 @@ static hipError_t launch_linear_prepare_t(const uint16_t* k, const uint16_t* v, 
   const LinearPtrs lp = linear_ws_ptrs(ws, BH, nb, D);
   if constexpr (D == 128 && BLK == 128) {
     const int npairs = (nb + 1) / 2;
-    lstate::lin_state_pipe_kernel<<<dim3((unsigned)(BH * npairs)), lstate::NT, 0, s>>>(
+    lstate::lin_state_pipe_kernel<false><<<dim3((unsigned)(BH * npairs)), lstate::NT, 0, s>>>(
         k, v, N, nb, npairs, lp.Ht, lp.Zs);
   } else {
     lin_state_kernel<D, BLK><<<dim3((unsigned)(BH * nb)), 256, 0, s>>>(k, v, N, nb, lp.Ht, lp.Zs);
@@ -615,29 +652,64 @@ static hipError_t launch_linear_prepare_t(const uint16_t* k, const uint16_t* v, 
   return launch_gather(lp.Ht, lp.bits, BH, nb, lp.words, D, lp.C, s);
 }
 
-template <int D, int WAVES>
-static void launch_gather_t(const uint16_t* Ht, const uint32_t* bits, int64_t BH, int nb, int W,
-                            uint16_t* C, hipStream_t s) {
+template <int D, int WAVES, bool HILO>
+static void launch_gather_t(const uint16_t* Ht, const uint16_t* Ht_lo, const uint32_t* bits,
+                            int64_t BH, int nb, int W, uint16_t* C, uint16_t* C_lo, hipStream_t s) {
   const int rowtiles = (nb + 64 * WAVES - 1) / (64 * WAVES), coltiles = D * D / 128;
   const int64_t tiles = BH * rowtiles * coltiles;
   const int per_xcd = (int)((tiles + 7) / 8);
-  lin_gather_kernel<D, WAVES><<<dim3((unsigned)(per_xcd * 8)), WAVES * 64, 0, s>>>(
-      Ht, bits, nb, nb, W, rowtiles, coltiles, per_xcd, tiles, C);
+  lin_gather_kernel<D, WAVES, HILO><<<dim3((unsigned)(per_xcd * 8)), WAVES * 64, 0, s>>>(
+      Ht, Ht_lo, bits, nb, nb, W, rowtiles, coltiles, per_xcd, tiles, C, C_lo);
 }
 
-hipError_t launch_gather(const uint16_t* Ht, const uint32_t* bits, int64_t BH, int nb, int W, int d,
-                         uint16_t* C, hipStream_t s) {
+template <bool HILO>
+static hipError_t launch_gather_any(const uint16_t* Ht, const uint16_t* Ht_lo, const uint32_t* bits,
+                                    int64_t BH, int nb, int W, int d, uint16_t* C, uint16_t* C_lo,
+                                    hipStream_t s) {
   // Row tiles of 256 query blocks (4 waves; two workgroups fill a CU's wave
   // slots), or of 128 when there are no more query blocks than that.  At the
   // 245,760-token layer 256-row tiles ran in 6.56 ms against 6.86 ms for 192
   // rows (no padding but 3/4 of the wave slots) and 6.59 ms for 512.
   if (d == 128) {
-    if (nb > 128) launch_gather_t<128, 4>(Ht, bits, BH, nb, W, C, s);
-    else launch_gather_t<128, 2>(Ht, bits, BH, nb, W, C, s);
+    if (nb > 128) launch_gather_t<128, 4, HILO>(Ht, Ht_lo, bits, BH, nb, W, C, C_lo, s);
+    else launch_gather_t<128, 2, HILO>(Ht, Ht_lo, bits, BH, nb, W, C, C_lo, s);
   } else {
-    if (nb > 128) launch_gather_t<64, 4>(Ht, bits, BH, nb, W, C, s);
-    else launch_gather_t<64, 2>(Ht, bits, BH, nb, W, C, s);
+    if (nb > 128) launch_gather_t<64, 4, HILO>(Ht, Ht_lo, bits, BH, nb, W, C, C_lo, s);
+    else launch_gather_t<64, 2, HILO>(Ht, Ht_lo, bits, BH, nb, W, C, C_lo, s);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const uint16_t* Ht, const uint32_t* bits, int64_t BH, int nb, int W, int d,
+                         uint16_t* C, hipStream_t s) {
+  return launch_gather_any<false>(Ht, nullptr, bits, BH, nb, W, d, C, nullptr, s);
+}
+
+hipError_t launch_gather_hilo(const uint16_t* Ht, const uint16_t* Ht_lo, const uint32_t* bits,
+                              int64_t BH, int nb, int W, int d, uint16_t* C, uint16_t* C_lo,
+                              hipStream_t s) {
+  return launch_gather_any<true>(Ht, Ht_lo, bits, BH, nb, W, d, C, C_lo, s);
+}
+
+template <int D, int BLK>
+static void launch_states_lo_t(const uint16_t* k, const uint16_t* v, int64_t BH, int N, int nb,
+                               uint16_t* Ht_lo, hipStream_t s) {
+  if constexpr (D == 128 && BLK == 128) {
+    const int npairs = (nb + 1) / 2;
+    lstate::lin_state_pipe_kernel<true><<<dim3((unsigned)(BH * npairs)), lstate::NT, 0, s>>>(
+        k, v, N, nb, npairs, Ht_lo, nullptr);
+  } else {
+    lin_state_kernel<D, BLK, true><<<dim3((unsigned)(BH * nb)), 256, 0, s>>>(k, v, N, nb, Ht_lo,
+                                                                             nullptr);
+  }
+}
+
+hipError_t launch_linear_states_lo(const uint16_t* k, const uint16_t* v, int64_t BH, int N, int d,
+                                   int block, int nb, uint16_t* Ht_lo, hipStream_t s) {
+  if (d == 128 && block == 128) launch_states_lo_t<128, 128>(k, v, BH, N, nb, Ht_lo, s);
+  else if (d == 128 && block == 64) launch_states_lo_t<128, 64>(k, v, BH, N, nb, Ht_lo, s);
+  else if (d == 64 && block == 128) launch_states_lo_t<64, 128>(k, v, BH, N, nb, Ht_lo, s);
+  else launch_states_lo_t<64, 64>(k, v, BH, N, nb, Ht_lo, s);
   return hipGetLastError();
 }
 

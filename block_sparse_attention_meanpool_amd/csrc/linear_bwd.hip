@@ -1,7 +1,8 @@
 // Backward pass of the linear-attention branch with the class map held fixed
 // (SLA post: intermediate blocks via linear attention, phi = elu + 1; results:
-// the method is trainable).  With a = phi(q), S_i, zeta_i from the forward's
-// prepared workspace, w_n = a_n . zeta_i and O_lin_n = a_n^T S_i / w_n:
+// the method is trainable).  With a = phi(q), zeta_i from the forward's
+// prepared workspace, S_i gathered again as a hi + lo bf16 pair (the states'
+// low parts recomputed here), w_n = a_n . zeta_i and O_lin_n = a_n^T S_i / w_n:
 //   g_n = dO_n / w_n,  h_n = -(dO_n . O_lin_n) / w_n
 //   dq_n  += (S_i g_n + zeta_i h_n) * phi'(q_n)
 //   dS_i   = A_i^T G_i,  dzeta_i = A_i^T h          (query side, per block)
@@ -45,13 +46,19 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
-// One workgroup per query block, 4 waves of 32 queries.
+// One workgroup per query block, 4 waves of 32 queries.  dq_n is the sum of
+// S_i g_n and zeta_i h_n, two terms that nearly cancel (exactly, when every
+// marginal value row is the same vector), so every factor that is rounded in
+// one term and not in the other enters as a hi + lo bf16 pair: S_i (C, C_lo,
+// from the backward's own gather), O_lin inside h (linear_apply on that pair)
+// and g.  The error is then about 2^-16 of the terms instead of 2^-9.
 __global__ __launch_bounds__(NT) void lin_bwd_query_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ d_o, int N, int nqb,
-    const uint16_t* __restrict__ C, const float* __restrict__ zeta, float* __restrict__ dq,
-    uint16_t* __restrict__ dS, float* __restrict__ dzeta) {
-  __shared__ __attribute__((aligned(1024))) char SB[D * 256];    // S_i^T rows e, then G rows n
-  __shared__ __attribute__((aligned(1024))) char AB[BLK * 256];  // phi(Q) rows n
+    const uint16_t* __restrict__ C, const uint16_t* __restrict__ C_lo,
+    const float* __restrict__ zeta, float* __restrict__ dq, uint16_t* __restrict__ dS,
+    float* __restrict__ dzeta) {
+  __shared__ __attribute__((aligned(1024))) char SB[D * 256];    // S_i^T hi rows e, then G rows n
+  __shared__ __attribute__((aligned(1024))) char AB[BLK * 256];  // S_i^T lo rows e, then phi(Q) rows n
   __shared__ float hs[BLK];
   const int64_t bh = blockIdx.x / nqb;
   const int qb = blockIdx.x % nqb;
@@ -62,8 +69,10 @@ __global__ __launch_bounds__(NT) void lin_bwd_query_kernel(
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(d_o + head_off, (uint32_t)N * D * 2);
   const int64_t row = bh * nqb + qb;
   const uint16_t* St = C + row * D * D;
+  const uint16_t* St_lo = C_lo + row * D * D;
   const float* zt = zeta + row * D;
   stage_tile(St, SB, lane, w);
+  stage_tile(St_lo, AB, lane, w);
 
   const int n = 32 * w + l32;  // query within the block
   const int qrow = qb * BLK + n;
@@ -74,7 +83,7 @@ __global__ __launch_bounds__(NT) void lin_bwd_query_kernel(
   float hdot = 0.f;
   {
     f32x16 acc[4];
-    linv = linear_apply<D>(St, zt, qf, l32, hf, acc);  // acc * linv = O_lin^T
+    linv = linear_apply<D, true>(St, zt, qf, l32, hf, acc, St_lo);  // acc * linv = O_lin^T
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -88,29 +97,37 @@ __global__ __launch_bounds__(NT) void lin_bwd_query_kernel(
   }
   hdot = sum_halves(hdot);
   const float hn = -hdot * linv * linv;  // -(dO . O_lin) / w
-  // g_n = dO_n / w_n as the B operand (bf16); phi(q_n) rows into LDS
-  u32x4 gb[8];
+  // g_n = dO_n / w_n as the B operand: a hi + lo bf16 pair
+  u32x4 gb[8], gl[8];
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     const u32x4 x = buf_load16(rdo, (uint32_t)(qrow * D + 16 * ks + 8 * hf) * 2);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      gb[ks][e] = pack_bf16x2(bf16_bits_to_f32(x[e] & 0xffffu) * linv,
-                              bf16_bits_to_f32(x[e] >> 16) * linv);
-    *(u32x4*)row_chunk(AB, n, 2 * ks + hf) = phi8(qf[ks], true);
+    for (int e = 0; e < 4; ++e) {
+      const float g0 = bf16_bits_to_f32(x[e] & 0xffffu) * linv;
+      const float g1 = bf16_bits_to_f32(x[e] >> 16) * linv;
+      gb[ks][e] = pack_bf16x2(g0, g1);
+      gl[ks][e] = pack_bf16x2_lo(g0, g1);
+    }
   }
   if (hf == 0) hs[n] = hn;
   wait_vmcnt0();
-  __syncthreads();  // S_i^T staged; phi(Q) rows and h written
+  __syncthreads();  // S_i^T hi and lo staged; h written
 
-  // da^T = S_i G^T: A = S_i [c x e] by transposed reads of the S_i^T rows
+  // da^T = S_i G^T: A = S_i [c x e] by transposed reads of the S_i^T rows,
+  // hi g_hi + hi g_lo + lo g_hi (the lo lo product is below 2^-16)
   {
     f32x16 dacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb)
-        dacc[cb] = mfma32x32x16(tr_operand<DualSwz>(SB, 16 * ks, 32 * cb, lane), gb[ks], dacc[cb]);
+      for (int cb = 0; cb < 4; ++cb) {
+        const u32x4 sh = tr_operand<DualSwz>(SB, 16 * ks, 32 * cb, lane);
+        const u32x4 sl = tr_operand<DualSwz>(AB, 16 * ks, 32 * cb, lane);
+        dacc[cb] = mfma32x32x16(sh, gb[ks], dacc[cb]);
+        dacc[cb] = mfma32x32x16(sh, gl[ks], dacc[cb]);
+        dacc[cb] = mfma32x32x16(sl, gb[ks], dacc[cb]);
+      }
     if (qrow < N) {
       float* drow = dq + head_off + (int64_t)qrow * D;
 #pragma unroll
@@ -130,8 +147,12 @@ __global__ __launch_bounds__(NT) void lin_bwd_query_kernel(
     }
   }
   __syncthreads();  // every wave is done reading S_i^T
+  // G rows (g rounded to bf16: dS_i has no cancelling terms) and phi(Q) rows
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) *(u32x4*)row_chunk(SB, n, 2 * ks + hf) = gb[ks];
+  for (int ks = 0; ks < 8; ++ks) {
+    *(u32x4*)row_chunk(SB, n, 2 * ks + hf) = gb[ks];
+    *(u32x4*)row_chunk(AB, n, 2 * ks + hf) = phi8(qf[ks], true);
+  }
   __syncthreads();
 
   // dS_i [c x e] = A^T G over the block's queries: 16 blocks of 32 x 32, 4 per wave
@@ -253,7 +274,8 @@ LinearBwdWs linear_bwd_ws_layout(int64_t BH, int nb, int D) {
   w.bits_bytes = up((size_t)BH * nb * w.words * 4);
   w.dh_bytes = up((size_t)BH * nb * D * D * 2);
   w.dz_bytes = up((size_t)BH * nb * D * 4);
-  w.total = w.ds_bytes + w.dzeta_bytes + w.bits_bytes + w.dh_bytes + w.dz_bytes;
+  w.lo_bytes = up((size_t)BH * nb * D * D * 2);
+  w.total = w.ds_bytes + w.dzeta_bytes + w.bits_bytes + w.dh_bytes + w.dz_bytes + 3 * w.lo_bytes;
   return w;
 }
 
@@ -274,14 +296,27 @@ hipError_t launch_linear_bwd(const uint16_t* q, const uint16_t* k, const uint16_
   uint16_t* dH = reinterpret_cast<uint16_t*>(p);
   p += lw.dh_bytes;
   float* dz = reinterpret_cast<float*>(p);
+  p += lw.dz_bytes;
+  uint16_t* Ht_lo = reinterpret_cast<uint16_t*>(p);
+  p += lw.lo_bytes;
+  uint16_t* Ch = reinterpret_cast<uint16_t*>(p);
+  p += lw.lo_bytes;
+  uint16_t* Cl = reinterpret_cast<uint16_t*>(p);
 
+  // S_i to about 16 bits for the query side: the states' low parts (the high
+  // parts are the prepared workspace's states), then the gather on the pair
+  hipError_t e = launch_linear_states_lo(k, v, BH, N, D, block, nb, Ht_lo, s);
+  if (e != hipSuccess) return e;
+  e = launch_gather_hilo(lp.Ht, Ht_lo, lp.bits, BH, nb, lp.words, D, Ch, Cl, s);
+  if (e != hipSuccess) return e;
   const dim3 grid((unsigned)(BH * nb));
-  hipError_t e;
   if (tuned) {
-    lbwd::lin_bwd_query_kernel<<<grid, lbwd::NT, 0, s>>>(q, d_o, N, nb, lp.C, lp.zeta, dq, dS, dzeta);
+    lbwd::lin_bwd_query_kernel<<<grid, lbwd::NT, 0, s>>>(q, d_o, N, nb, Ch, Cl, lp.zeta, dq, dS,
+                                                         dzeta);
     e = hipGetLastError();
   } else {
-    e = launch_linear_bwd_query_generic(q, d_o, BH, N, D, block, nb, lp.C, lp.zeta, dq, dS, dzeta, s);
+    e = launch_linear_bwd_query_generic(q, d_o, BH, N, D, block, nb, Ch, Cl, lp.zeta, dq, dS,
+                                        dzeta, s);
   }
   if (e != hipSuccess) return e;
   e = launch_col_bits(idx, cnt, kmax, BH, nb, nb, lw.words, bitsT, s);

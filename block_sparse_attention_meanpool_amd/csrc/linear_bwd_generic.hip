@@ -40,13 +40,17 @@ struct ScaleChunk {  // the 8 values times a per-row factor, rounded to bf16 (as
 };
 
 // One workgroup per query block, BLK/32 waves of 32 queries (one per lane).
+// As in the tuned kernel, dq's two nearly cancelling terms get S_i (C, C_lo),
+// O_lin and g as hi + lo bf16 pairs.
 template <int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) void query_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ d_o, int N, int nqb,
-    const uint16_t* __restrict__ C, const float* __restrict__ zeta, float* __restrict__ dq,
-    uint16_t* __restrict__ dS, float* __restrict__ dzeta) {
+    const uint16_t* __restrict__ C, const uint16_t* __restrict__ C_lo,
+    const float* __restrict__ zeta, float* __restrict__ dq, uint16_t* __restrict__ dS,
+    float* __restrict__ dzeta) {
   constexpr int NT = BLK * 2, W = BLK / 32, KS = D / 16, DB = D / 32;
   __shared__ __attribute__((aligned(16))) char Sr[D * D * 2];    // S_i: rows c, e contiguous
+  __shared__ __attribute__((aligned(16))) char Sl[D * D * 2];    // its low part, same layout
   __shared__ __attribute__((aligned(16))) char At[D * BLK * 2];  // phi(Q)^T: rows c, n contiguous
   __shared__ __attribute__((aligned(16))) char Gt[D * BLK * 2];  // G^T: rows e, n contiguous
   __shared__ float winv[BLK], hs[BLK];
@@ -59,6 +63,7 @@ __global__ __launch_bounds__(BLK * 2) void query_kernel(
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(d_o + head_off, (uint32_t)N * D * 2);
   const int64_t row = bh * nqb + qb;
   const uint16_t* St = C + row * D * D;  // S_i^T: row e holds c = 0..D-1
+  const uint16_t* St_lo = C_lo + row * D * D;
   const float* zt = zeta + row * D;
   const int n = 32 * w + l32;  // query within the block
   const int qrow = qb * BLK + n;
@@ -69,7 +74,7 @@ __global__ __launch_bounds__(BLK * 2) void query_kernel(
   float linv, hdot = 0.f;
   {
     f32x16 acc[DB];
-    linv = linear_apply<D>(St, zt, qf, l32, hf, acc);  // acc * linv = O_lin^T
+    linv = linear_apply<D, true>(St, zt, qf, l32, hf, acc, St_lo);  // acc * linv = O_lin^T
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -90,15 +95,19 @@ __global__ __launch_bounds__(BLK * 2) void query_kernel(
     winv[n] = linv;
     hs[n] = hn;
   }
-  // g_n = dO_n / w_n as the B operand (bf16): lane holds g[n][16 ks + 8 hf + 0..7]
-  u32x4 gb[KS];
+  // g_n = dO_n / w_n as the B operand, a hi + lo bf16 pair: lane holds
+  // g[n][16 ks + 8 hf + 0..7]
+  u32x4 gb[KS], gl[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
     const u32x4 x = buf_load16(rdo, (uint32_t)(qrow * D + 16 * ks + 8 * hf) * 2);
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      gb[ks][e] = pack_bf16x2(bf16_bits_to_f32(x[e] & 0xffffu) * linv,
-                              bf16_bits_to_f32(x[e] >> 16) * linv);
+    for (int e = 0; e < 4; ++e) {
+      const float g0 = bf16_bits_to_f32(x[e] & 0xffffu) * linv;
+      const float g1 = bf16_bits_to_f32(x[e] >> 16) * linv;
+      gb[ks][e] = pack_bf16x2(g0, g1);
+      gl[ks][e] = pack_bf16x2_lo(g0, g1);
+    }
   }
   __syncthreads();  // winv and hs written
   // S_i (the transpose of the stored S_i^T), phi(Q)^T and G^T into LDS; the
@@ -107,13 +116,15 @@ __global__ __launch_bounds__(BLK * 2) void query_kernel(
   const uint32_t blk_bytes = (uint32_t)valid * D * 2;
   const int64_t blk_off = head_off + (int64_t)qb * BLK * D;
   stage_subblocks<D, D, NT>(make_rsrc(St, D * D * 2), 0, nullptr, Sr, tid, KeepChunk{});
+  stage_subblocks<D, D, NT>(make_rsrc(St_lo, D * D * 2), 0, nullptr, Sl, tid, KeepChunk{});
   stage_subblocks<BLK, D, NT>(make_rsrc(q + blk_off, blk_bytes), 0, nullptr, At, tid,
                               PhiChunk{valid});
   stage_subblocks<BLK, D, NT>(make_rsrc(d_o + blk_off, blk_bytes), 0, nullptr, Gt, tid,
                               ScaleChunk{winv});
   __syncthreads();
 
-  // da^T = S_i G^T: A = S_i [c x e] rows from Sr, B = G^T from registers
+  // da^T = S_i G^T: A = S_i [c x e] rows from Sr (and Sl), B = G^T from
+  // registers; hi g_hi + hi g_lo + lo g_hi
   {
     f32x16 dacc[DB];
 #pragma unroll
@@ -121,9 +132,13 @@ __global__ __launch_bounds__(BLK * 2) void query_kernel(
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-      for (int cb = 0; cb < DB; ++cb)
-        dacc[cb] = mfma32x32x16(*(const u32x4*)(Sr + tr_offset<D>(32 * cb + l32, 2 * ks + hf)),
-                                gb[ks], dacc[cb]);
+      for (int cb = 0; cb < DB; ++cb) {
+        const uint32_t off = tr_offset<D>(32 * cb + l32, 2 * ks + hf);
+        const u32x4 sh = *(const u32x4*)(Sr + off), sl = *(const u32x4*)(Sl + off);
+        dacc[cb] = mfma32x32x16(sh, gb[ks], dacc[cb]);
+        dacc[cb] = mfma32x32x16(sh, gl[ks], dacc[cb]);
+        dacc[cb] = mfma32x32x16(sl, gb[ks], dacc[cb]);
+      }
     if (qrow < N) {
       float* drow = dq + head_off + (int64_t)qrow * D;
 #pragma unroll
@@ -263,15 +278,15 @@ __global__ __launch_bounds__(BLK * 2) void key_kernel(const uint16_t* __restrict
 
 hipError_t launch_linear_bwd_query_generic(const uint16_t* q, const uint16_t* d_o, int64_t BH,
                                            int N, int d, int block, int nb, const uint16_t* C,
-                                           const float* zeta, float* dq, uint16_t* dS,
-                                           float* dzeta, hipStream_t s) {
+                                           const uint16_t* C_lo, const float* zeta, float* dq,
+                                           uint16_t* dS, float* dzeta, hipStream_t s) {
   const dim3 grid((unsigned)(BH * nb));
   if (d == 64 && block == 64)
-    glbwd::query_kernel<64, 64><<<grid, 128, 0, s>>>(q, d_o, N, nb, C, zeta, dq, dS, dzeta);
+    glbwd::query_kernel<64, 64><<<grid, 128, 0, s>>>(q, d_o, N, nb, C, C_lo, zeta, dq, dS, dzeta);
   else if (d == 64 && block == 128)
-    glbwd::query_kernel<64, 128><<<grid, 256, 0, s>>>(q, d_o, N, nb, C, zeta, dq, dS, dzeta);
+    glbwd::query_kernel<64, 128><<<grid, 256, 0, s>>>(q, d_o, N, nb, C, C_lo, zeta, dq, dS, dzeta);
   else if (d == 128 && block == 64)
-    glbwd::query_kernel<128, 64><<<grid, 128, 0, s>>>(q, d_o, N, nb, C, zeta, dq, dS, dzeta);
+    glbwd::query_kernel<128, 64><<<grid, 128, 0, s>>>(q, d_o, N, nb, C, C_lo, zeta, dq, dS, dzeta);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

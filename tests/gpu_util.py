@@ -25,6 +25,12 @@ REL_L2 = 5e-3
 # relative, and ln(sum) by at most ln(1 + 2^-8) < 2^-8, plus fp32 error.
 BF16_U = 2.0 ** -8
 LSE_MAX_ABS = BF16_U + 5e-4
+# The LSE error is the log of the normaliser's relative error, a weighted mean
+# sum_i w_i delta_i of the roundings (weights w_i = p_i / sum p, |delta_i| <=
+# 2^-8, independent, mean square at most 2^-16 / 3); its mean square is at
+# most (2^-16 / 3) sum_i w_i^2 <= 2^-16 / 3.  So the root-mean-square error
+# over the rows is held to 2^-8 / sqrt(3), plus the same fp32 slack scaled down.
+LSE_RMS = BF16_U / math.sqrt(3.0) + 1e-4
 
 
 def say(*a):
@@ -73,6 +79,24 @@ def check_close(got, want, what, max_abs=MAX_ABS, rel_l2=REL_L2):
     assert mabs <= max_abs, f"{what}: max-abs {mabs} > {max_abs}"
     assert rel <= rel_l2, f"{what}: rel-L2 {rel} > {rel_l2}"
     return mabs, rel
+
+
+def check_lse(got, want, what="LSE"):
+    """LSE against the oracle: every finite entry within LSE_MAX_ABS, their
+    root-mean-square error within LSE_RMS; -inf exactly where the oracle has it."""
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(got), fin), f"{what}: -inf rows differ"
+    assert (got[~fin] == want[~fin]).all(), f"{what}: non-finite values differ"
+    diff = got[fin] - want[fin]
+    mabs = float(np.abs(diff).max()) if diff.size else 0.0
+    rms = float(np.sqrt(np.mean(diff ** 2))) if diff.size else 0.0
+    say(f"  {what}: max|d| = {mabs:.3e}, rms = {rms:.3e} (bars {LSE_MAX_ABS:.2e}, {LSE_RMS:.2e})")
+    assert mabs <= LSE_MAX_ABS, f"{what}: max-abs {mabs} > {LSE_MAX_ABS}"
+    assert rms <= LSE_RMS, f"{what}: rms {rms} > {LSE_RMS}"
+    return mabs, rms
 
 
 def rne_bf16_bits(x32):

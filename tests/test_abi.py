@@ -104,9 +104,10 @@ def test_workspace_sizes(mod):
     for d, b in ((64, 64), (128, 64)):
         assert lib.sla_sparse_attn_bwd_ws_bytes(1, 2, 1024, d, b) == 8192 + 256 + 256 + 1024
     # linear backward: dS_i and dH_j bf16 [2, 16, d*d], dzeta_i and dz_j fp32 [2, 16, d],
-    # column bits [2, 16, 2 words]
+    # column bits [2, 16, 2 words], then the states' low parts and S_i as a hi + lo
+    # pair, bf16 [2, 16, d*d] each
     assert lib.sla_linear_branch_bwd_ws_bytes(1, 2, 1024, 64, 64) == \
-        2 * (2 * 16 * 64 * 64 * 2) + 2 * (2 * 16 * 64 * 4) + 256
+        2 * (2 * 16 * 64 * 64 * 2) + 2 * (2 * 16 * 64 * 4) + 256 + 3 * (2 * 16 * 64 * 64 * 2)
     assert lib.sla_linear_branch_bwd_ws_bytes(1, 2, 1024, 96, 64) == 0
 
 

@@ -2,13 +2,16 @@
 fp64 gradients (oracle/grad.py), through the C ABI.
 
 Bars.  A gradient entry is a sum of products in which one factor (P or dS)
-is rounded to bf16 (unit roundoff 2^-8, so at most 2^-9 relative after
-rounding to nearest) and everything else is exact bf16 input or fp32
-accumulation; the rounding errors are independent, so the sum's error is a
-few times 2^-9 of the magnitude of its terms.  The output bars (rel-L2 5e-3,
-max-abs 2e-2) are therefore kept, with the max-abs bar taken relative to the
-gradient's scale: |got - ref| <= 2e-2 * max(1, max |ref|), since dK and dV
-sum over every query that attends a key and grow with that count.
+is rounded to bf16 (unit roundoff 2^-8) and everything else is exact bf16
+input or fp32 accumulation; the rounding errors are independent, so the sum's
+error is a few times 2^-9 of the magnitude of its terms.  The output bars
+(rel-L2 5e-3, max-abs 2e-2) are therefore kept for every gradient, with the
+max-abs bar taken relative to the gradient's scale:
+|got - ref| <= 2e-2 * max(1, max |ref|), since dK and dV sum over every query
+that attends a key and grow with that count.  The linear branch's dQ is the
+difference of two terms that nearly cancel; the kernels give every factor
+that enters one term rounded and the other not (S_i, O_lin, g) as a hi + lo
+bf16 pair, so it is held to the same bars.
 """
 
 from fractions import Fraction as F
@@ -37,20 +40,22 @@ def _grad_close(got, want, what, rel_l2=REL_L2):
     return check_close(got, want, what, max_abs=MAX_ABS * scale, rel_l2=rel_l2)
 
 
-# The linear branch's dQ is the difference of two terms that nearly cancel
-# (oracle.grad.linear_dq_scale), and S_i and g enter the MFMA in bf16: each
-# rounding is at most 2^-9 of a term, so the error of dQ is measured against
-# the size of the terms: |got - ref|_2 <= 5e-3 |ref|_2 + 2^-9 |terms|_2.
-LIN_TERM_BAR = 2.0 ** -9
+def _rel_for(o_fp32):
+    """The rel-L2 bar for a softmax-branch backward given O_s in fp32 (what the
+    forward can write and the autograd form saves) or in bf16.  A bf16 O_s is
+    an input of lower precision: D_n = dO_n . O_s_n then carries its rounding
+    (up to 2^-9 |dO_n| |O_n|), and D enters every dS of the row, so dQ and dK
+    inherit an error of the size of the rounding of O itself.  That input mode
+    alone doubles the rel-L2 bar; every kernel-side rounding is held to 5e-3."""
+    return REL_L2 if o_fp32 else 2 * REL_L2
 
 
 def _dq_close(got, want, terms, what):
-    err = float(np.linalg.norm(got - want))
-    ref, size = float(np.linalg.norm(want)), float(np.linalg.norm(terms))
-    say(f"  {what}: |err| = {err:.3e}, |ref| = {ref:.3e}, |terms| = {size:.3e}, "
-        f"|err| / |terms| = {err / max(size, 1e-30):.3e}")
-    _grad_close(got, want, what, rel_l2=np.inf)  # the max-abs bar
-    assert err <= REL_L2 * ref + LIN_TERM_BAR * size, f"{what}: {err} > bar"
+    """dQ at the plain bars; also prints how far below the size of its two
+    cancelling terms (oracle.grad.linear_dq_scale) the error lies."""
+    err, size = float(np.linalg.norm(got - want)), float(np.linalg.norm(terms))
+    say(f"  {what}: |err| / |terms| = {err / max(size, 1e-30):.3e}")
+    _grad_close(got, want, what)
 
 
 def _mask(nb, H, seed, dense_frac=0.35):
@@ -90,12 +95,8 @@ def test_softmax_backward_small(o_fp32):
     say(f"[backward] softmax branch, N=1000 (ragged), o_s fp32={o_fp32}")
     cls = _mask(SPEC.nb, SPEC.H, 11)
     got, ref = _run(SPEC, cls, o_fp32)
-    # With a bf16 O_s, D_n = dO_n . O_s_n carries that rounding too (up to
-    # 2^-9 sum |dO| |O| per row, entering every dS of the row): the rel-L2
-    # bar doubles for that variant.
-    rel = REL_L2 if o_fp32 else 2 * REL_L2
     for a, b, n in zip(got, ref, ("dQ", "dK", "dV")):
-        _grad_close(a, b, n, rel_l2=rel)
+        _grad_close(a, b, n, rel_l2=_rel_for(o_fp32))
     # the key tile no query block uses and the row with no tile get exactly nothing
     assert not got[1][0, 1, 3 * 128:4 * 128].any() and not got[2][0, 1, 3 * 128:4 * 128].any()
     assert not got[0][0, 0, 128:256].any()
@@ -117,9 +118,8 @@ def test_softmax_backward_other_shapes(d, block, N):
         cls[0, 0, 0] = osla.CRITICAL
     for o_fp32 in (True, False):
         got, ref = _run(spec, cls, o_fp32)
-        rel = REL_L2 if o_fp32 else 2 * REL_L2
         for a, b, n in zip(got, ref, ("dQ", "dK", "dV")):
-            _grad_close(a, b, f"{n} o_s fp32={o_fp32}", rel_l2=rel)
+            _grad_close(a, b, f"{n} o_s fp32={o_fp32}", rel_l2=_rel_for(o_fp32))
     if nb >= 5:
         # the key tile no query block uses and the row with no tile get exactly nothing
         assert not got[1][0, 1, 3 * block:4 * block].any() and not got[2][0, 1, 3 * block:4 * block].any()

@@ -72,8 +72,6 @@ def test_backward_small_lengths(N, d, block):
     torch.cuda.synchronize()
     f64 = [osla.bf16_to_f64(x) for x in bits]
     ref = ograd.backward(*f64[:3], cls, block, f64[3])
-    # the linear dQ errs in proportion to the size of its two cancelling terms
-    terms = ograd.linear_dq_scale(*f64[:3], cls, block, f64[3])
     for t, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
         got = t.cpu().numpy()
         if np.abs(r).max() < 1e-9:
@@ -84,13 +82,7 @@ def test_backward_small_lengths(N, d, block):
             assert np.abs(got).max() <= MAX_ABS
             continue
         scale = max(1.0, float(np.abs(r).max()))
-        if n == "dQ":
-            err, size = float(np.linalg.norm(got - r)), float(np.linalg.norm(terms))
-            say(f"  dQ: |err| = {err:.3e}, |ref| = {np.linalg.norm(r):.3e}, |terms| = {size:.3e}")
-            assert err <= 2 * REL_L2 * float(np.linalg.norm(r)) + 2.0 ** -9 * size
-            check_close(got, r, f"{n} N={N}", max_abs=MAX_ABS * scale, rel_l2=np.inf)
-        else:
-            check_close(got, r, f"{n} N={N}", max_abs=MAX_ABS * scale, rel_l2=2 * REL_L2)
+        check_close(got, r, f"{n} N={N}", max_abs=MAX_ABS * scale, rel_l2=REL_L2)
 
 
 def _ramp_inputs(nb, block=128, d=128, seed=0):

@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import block_sparse_attention_meanpool_amd as sla
-from gpu_util import (LSE_MAX_ABS, REL_L2, bits_of, check_close, counts, f64, rne_bf16_bits, say, small_inputs, to_dev)
+from gpu_util import (REL_L2, bits_of, check_close, check_lse, counts, f64, rne_bf16_bits, say, small_inputs, to_dev)
 from oracle import sla as osla
 from synth.configs import Spec
 
@@ -107,7 +107,7 @@ def test_lists_bit_exact(case):
 def test_sparse_branch(case):
     o_s_ref, lse_ref, _, _ = case["ref"]
     check_close(case["o_s"], o_s_ref, "O_s")
-    check_close(case["lse"], lse_ref, "LSE", max_abs=LSE_MAX_ABS, rel_l2=REL_L2)
+    check_lse(case["lse"], lse_ref)
     # the bf16-output mode of the same kernel is the RNE rounding of its fp32 output
     np.testing.assert_array_equal(case["o_s16"], rne_bf16_bits(case["o_s"]))
 
