@@ -9,6 +9,7 @@ from .binding import (CLS_CRITICAL, CLS_MARGINAL, CLS_SKIP, EXPORTS, FLAG_BAD_CL
                       forward, lib, num_blocks, sla_attention, sla_block_mask, sla_combine,
                       sla_dense_attn_fwd, sla_linear_branch_bwd, sla_linear_branch_fwd,
                       sla_linear_branch_prepare, sla_mask_recall, sla_pool_classify,
+                      sla_pool_classify_noalloc,
                       sla_sparse_attn_bwd, sla_sparse_attn_fwd, sla_sparse_linear_attn_fwd,
                       sla_status_string, sla_tile_permute, sla_version)
 
@@ -17,5 +18,6 @@ __all__ = ["CLS_CRITICAL", "CLS_MARGINAL", "CLS_SKIP", "EXPORTS", "FLAG_BAD_CLAS
            "forward", "lib", "num_blocks", "sla_attention", "sla_block_mask", "sla_combine",
            "sla_dense_attn_fwd", "sla_linear_branch_bwd", "sla_linear_branch_fwd",
            "sla_linear_branch_prepare", "sla_mask_recall", "sla_pool_classify",
+           "sla_pool_classify_noalloc",
            "sla_sparse_attn_bwd", "sla_sparse_attn_fwd", "sla_sparse_linear_attn_fwd",
            "sla_status_string", "sla_tile_permute", "sla_version"]

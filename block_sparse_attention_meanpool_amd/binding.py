@@ -34,6 +34,9 @@ _SIGS = {
     "sla_pool_classify": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32, _F, _F,
                                  _P, _P, _P, _P, _SZ, _P]),
     "sla_pool_classify_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32, _I32]),
+    "sla_pool_classify_noalloc": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _I32, _I32, _I32,
+                                         _F, _F, _P, _P, _P, _P]),
+    "sla_pool_classify_noalloc_scratch_bytes": (_SZ, []),
     "sla_block_mask": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _I32, _P, _P]),
     "sla_sparse_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _F,
                                    _P, _I32, _P, _P]),
@@ -158,6 +161,25 @@ def sla_pool_classify(q, k, block, mode, k_crit=0, k_marg=0, thr=0.0, scale=None
     _call("sla_pool_classify", _ptr(q), _ptr(k), B, H, N, d, block, MODES.get(mode, mode),
           int(k_crit), int(k_marg), float(thr), float(scale), _ptr(q_pool), _ptr(k_pool),
           _ptr(cls), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
+    return cls
+
+
+def sla_pool_classify_noalloc(q, k, block, mode, k_crit=0, k_marg=0, thr=0.0, scale=None,
+                              q_pool=None, k_pool=None, cls=None, stream=None):
+    """sla_pool_classify without a workspace (the library's static device
+    scratch instead): for callers that cannot allocate.  Pass `cls` (and the
+    pooled outputs, if wanted) to make the whole call allocation-free."""
+    _dev(q, torch.bfloat16, "q")
+    _dev(k, torch.bfloat16, "k")
+    B, H, N, d = q.shape
+    nb = num_blocks(N, block)
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if cls is None:
+        cls = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=q.device)
+    _call("sla_pool_classify_noalloc", _ptr(q), _ptr(k), B, H, N, d, block, MODES.get(mode, mode),
+          int(k_crit), int(k_marg), float(thr), float(scale), _ptr(q_pool), _ptr(k_pool),
+          _ptr(cls), _stream(stream))
     return cls
 
 

@@ -39,6 +39,51 @@ size_t score_bytes(int64_t BH, int64_t nb) {
   return round_up((size_t)(BH * nb * nb) * sizeof(float), 256);
 }
 
+// Checks shared by sla_pool_classify and its allocation-free variant.
+sla_status check_pool_classify(const uint16_t* q, const uint16_t* k, int64_t nb, int32_t mode,
+                               int32_t k_crit, int32_t k_marg, float thr, float scale,
+                               const float* q_pool, const float* k_pool, const uint8_t* cls) {
+  if (!q || !k || !cls) return SLA_ERR_INVALID_ARG;
+  if ((q_pool == nullptr) != (k_pool == nullptr)) return SLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(q_pool) || !aligned16(k_pool))
+    return SLA_ERR_ALIGNMENT;
+  if (mode == SLA_SEL_TOPK || mode == SLA_SEL_SLA3) {
+    if (k_crit < 1 || k_crit > nb) return SLA_ERR_INVALID_ARG;
+    if (mode == SLA_SEL_SLA3 && (k_marg < 0 || k_marg > nb - k_crit)) return SLA_ERR_INVALID_ARG;
+  } else if (mode == SLA_SEL_CDF) {
+    if (!(thr > 0.f && thr < 1.f)) return SLA_ERR_INVALID_ARG;
+  } else {
+    return SLA_ERR_INVALID_ARG;
+  }
+  if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
+  return SLA_OK;
+}
+
+// Pool, score and select BH heads whose scratch (pooled Q/K unless given, then
+// the scores) starts at `scratch`.
+sla_status run_pool_classify(const uint16_t* q, const uint16_t* k, int64_t BH, int64_t N,
+                             int64_t d, int32_t block, int64_t nb, int32_t mode, int32_t k_crit,
+                             int32_t k_marg, float thr, float scale, float* q_pool, float* k_pool,
+                             uint8_t* cls, char* scratch, hipStream_t stream) {
+  char* p = scratch;
+  float* qp = q_pool;
+  float* kp = k_pool;
+  if (!qp) {
+    qp = reinterpret_cast<float*>(p);
+    kp = reinterpret_cast<float*>(p + pooled_bytes(BH, nb, d));
+    p += 2 * pooled_bytes(BH, nb, d);
+  }
+  float* S = reinterpret_cast<float*>(p);
+  const int kc = mode == SLA_SEL_CDF ? 0 : k_crit;
+  const int km = mode == SLA_SEL_SLA3 ? k_marg : 0;
+  sla_status st =
+      from_hip(sla::launch_pool(q, k, qp, kp, BH, (int)N, (int)d, block, (int)nb, stream));
+  if (st != SLA_OK) return st;
+  st = from_hip(sla::launch_scores(qp, kp, S, BH, (int)d, (int)nb, scale, stream));
+  if (st != SLA_OK) return st;
+  return from_hip(sla::launch_select(S, cls, BH * nb, (int)nb, mode, kc, km, thr, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -58,40 +103,47 @@ sla_status sla_pool_classify(const uint16_t* q, const uint16_t* k, int64_t B, in
   int64_t nb = 0;
   sla_status st = check_shape(B, H, N, d, block, &nb);
   if (st != SLA_OK) return st;
-  if (!q || !k || !cls) return SLA_ERR_INVALID_ARG;
-  if ((q_pool == nullptr) != (k_pool == nullptr)) return SLA_ERR_INVALID_ARG;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(q_pool) || !aligned16(k_pool))
-    return SLA_ERR_ALIGNMENT;
-  if (mode == SLA_SEL_TOPK || mode == SLA_SEL_SLA3) {
-    if (k_crit < 1 || k_crit > nb) return SLA_ERR_INVALID_ARG;
-    if (mode == SLA_SEL_SLA3 && (k_marg < 0 || k_marg > nb - k_crit)) return SLA_ERR_INVALID_ARG;
-  } else if (mode == SLA_SEL_CDF) {
-    if (!(thr > 0.f && thr < 1.f)) return SLA_ERR_INVALID_ARG;
-  } else {
-    return SLA_ERR_INVALID_ARG;
-  }
-  if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
-  const int64_t BH = B * H;
+  st = check_pool_classify(q, k, nb, mode, k_crit, k_marg, thr, scale, q_pool, k_pool, cls);
+  if (st != SLA_OK) return st;
   const size_t need = sla_pool_classify_ws_bytes(B, H, N, d, block, q_pool != nullptr);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  return run_pool_classify(q, k, B * H, N, d, block, nb, mode, k_crit, k_marg, thr, scale, q_pool,
+                           k_pool, cls, static_cast<char*>(ws), stream);
+}
 
-  char* p = static_cast<char*>(ws);
-  float* qp = q_pool;
-  float* kp = k_pool;
-  if (!qp) {
-    qp = reinterpret_cast<float*>(p);
-    kp = reinterpret_cast<float*>(p + pooled_bytes(BH, nb, d));
-    p += 2 * pooled_bytes(BH, nb, d);
+size_t sla_pool_classify_noalloc_scratch_bytes(void) { return sla::kNoallocScratchBytes; }
+
+sla_status sla_pool_classify_noalloc(const uint16_t* q, const uint16_t* k, int64_t B, int64_t H,
+                                     int64_t N, int64_t d, int32_t block, int32_t mode,
+                                     int32_t k_crit, int32_t k_marg, float thr, float scale,
+                                     float* q_pool, float* k_pool, uint8_t* cls,
+                                     hipStream_t stream) {
+  int64_t nb = 0;
+  sla_status st = check_shape(B, H, N, d, block, &nb);
+  if (st != SLA_OK) return st;
+  st = check_pool_classify(q, k, nb, mode, k_crit, k_marg, thr, scale, q_pool, k_pool, cls);
+  if (st != SLA_OK) return st;
+  // heads per pass: as many as the static scratch holds
+  const bool given = q_pool != nullptr;
+  auto need = [&](int64_t heads) {
+    return (given ? 0 : 2 * pooled_bytes(heads, nb, d)) + score_bytes(heads, nb);
+  };
+  if (need(1) > sla::kNoallocScratchBytes) return SLA_ERR_WORKSPACE;
+  const int64_t BH = B * H;
+  int64_t per = sla::kNoallocScratchBytes / need(1);
+  while (per > 1 && need(per) > sla::kNoallocScratchBytes) --per;
+  void* scratch = nullptr;
+  st = from_hip(sla::noalloc_scratch(&scratch));
+  if (st != SLA_OK) return st;
+  for (int64_t h0 = 0; h0 < BH; h0 += per) {
+    const int64_t c = per < BH - h0 ? per : BH - h0;
+    st = run_pool_classify(q + h0 * N * d, k + h0 * N * d, c, N, d, block, nb, mode, k_crit,
+                           k_marg, thr, scale, given ? q_pool + h0 * nb * d : nullptr,
+                           given ? k_pool + h0 * nb * d : nullptr, cls + h0 * nb * nb,
+                           static_cast<char*>(scratch), stream);
+    if (st != SLA_OK) return st;
   }
-  float* S = reinterpret_cast<float*>(p);
-  const int kc = mode == SLA_SEL_CDF ? 0 : k_crit;
-  const int km = mode == SLA_SEL_SLA3 ? k_marg : 0;
-
-  st = from_hip(sla::launch_pool(q, k, qp, kp, BH, (int)N, (int)d, block, (int)nb, stream));
-  if (st != SLA_OK) return st;
-  st = from_hip(sla::launch_scores(qp, kp, S, BH, (int)d, (int)nb, scale, stream));
-  if (st != SLA_OK) return st;
-  return from_hip(sla::launch_select(S, cls, BH * nb, (int)nb, mode, kc, km, thr, stream));
+  return SLA_OK;
 }
 
 sla_status sla_block_mask(const uint8_t* cls, int64_t B, int64_t H, int64_t nqb, int64_t nkb,

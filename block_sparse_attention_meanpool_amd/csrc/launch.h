@@ -132,5 +132,13 @@ hipError_t launch_tile_permute(const uint16_t* x, uint16_t* y, int64_t BH, int H
                                int X, int d, const TileShapes& ts, int inverse, hipStream_t s);
 hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,
                           int64_t n_elems, hipStream_t s);
+// Bytes of the static device scratch behind sla_pool_classify_noalloc: one
+// head's pooled Q and K and fp32 scores at the largest block count (4096
+// blocks, d = 128) fit, so every supported shape runs, a chunk of heads at a
+// time.
+constexpr size_t kNoallocScratchBytes = size_t(80) << 20;
+// Device address of that scratch on the current device (looked up once per
+// device, then cached).
+hipError_t noalloc_scratch(void** ptr);
 
 }  // namespace sla

@@ -26,8 +26,9 @@
  *   - Every call validates its arguments on the host first.  On an error it
  *     launches nothing, touches no output and returns a status < 0.
  *   - All work is enqueued asynchronously on `stream` (0 = the null stream).
- *     The library never allocates, frees or synchronises; it keeps no state
- *     and may be called from several host threads.
+ *     The library never allocates, frees or synchronises and may be called
+ *     from several host threads.  It keeps no state, except the static device
+ *     scratch of sla_pool_classify_noalloc (see there).
  *   - A HIP launch error is returned as SLA_ERR_HIP.  No C++ exception
  *     crosses this interface.
  *
@@ -97,6 +98,32 @@ sla_status sla_pool_classify(const uint16_t* q, const uint16_t* k, int64_t B, in
  * fp32 score matrix [B, H, nb, nb]).  Returns 0 for unsupported arguments. */
 size_t sla_pool_classify_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block,
                                   int32_t pooled_given);
+
+/*
+ * sla_pool_classify for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, rules and outputs as sla_pool_classify (the
+ * same kernels; bit-identical results), without the workspace: the pooled
+ * Q/K (unless q_pool/k_pool are given) and the scores live in a static
+ * device array of sla_pool_classify_noalloc_scratch_bytes() bytes (80 MiB)
+ * that the library holds on each GPU it runs on until the process ends.
+ * Heads are processed in chunks that fit that array; a shape whose single
+ * head does not fit is rejected with SLA_ERR_WORKSPACE (no supported shape
+ * is: one head at nb = 4096, d = 128 needs 71.3 MB).  The call allocates
+ * nothing and enqueues no memset.  On its first use on a device it looks the
+ * array's device address up once (with that device current).  Every call on
+ * one GPU shares the array: calls that overlap on one GPU (different
+ * streams, or host threads without ordering) race and must be serialised by
+ * the caller; calls in one stream are ordered.
+ */
+sla_status sla_pool_classify_noalloc(const uint16_t* q, const uint16_t* k, int64_t B, int64_t H,
+                                     int64_t N, int64_t d, int32_t block, int32_t mode,
+                                     int32_t k_crit, int32_t k_marg, float thr, float scale,
+                                     float* q_pool, float* k_pool, uint8_t* cls,
+                                     hipStream_t stream);
+
+/* Size in bytes of the static device array behind sla_pool_classify_noalloc. */
+size_t sla_pool_classify_noalloc_scratch_bytes(void);
 
 /*
  * Turn a class map into compact, ascending per-row lists of key blocks: the
