@@ -15,12 +15,15 @@ from fractions import Fraction
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsla.so")
+# SLA_LIBRARY selects another build of the same library (the debug-checks or
+# host-sanitized variants); the default is the in-tree release build.
+LIB_PATH = os.environ.get("SLA_LIBRARY") or os.path.join(_HERE, "libsla.so")
 
 SEL_TOPK, SEL_CDF, SEL_SLA3 = 0, 1, 2
 MODES = {"topk": SEL_TOPK, "cdf": SEL_CDF, "sla3": SEL_SLA3}
 CLS_SKIP, CLS_MARGINAL, CLS_CRITICAL = 0, 1, 2
 FLAG_BAD_CLASS, FLAG_OVERFLOW = 1, 2
+FLAG_LIST_RANGE, FLAG_LIST_REPEAT, FLAG_LIST_ORDER, FLAG_LIST_COUNT = 4, 8, 16, 32
 
 _lib = None
 
@@ -59,6 +62,8 @@ _SIGS = {
     "sla_mask_recall_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32]),
     "sla_tile_permute": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I32, _P]),
     "sla_dense_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _F, _P, _I32, _P, _P]),
+    "sla_check_lists": (_I32, [_P, _P, _I64, _I32, _I64, _P, _P]),
+    "sla_debug_flag": (_P, []),
     "sla_status_string": (ctypes.c_char_p, [_I32]),
     "sla_version": (_I32, []),
 }
@@ -111,14 +116,41 @@ def _call(name, *args):
         raise SlaError(name, st)
 
 
-def _dev(t, dtype, name):
+def _dev(t, dtype, name, device=None):
+    """A contiguous GPU tensor of `dtype` (or one of a tuple of dtypes), on
+    `device` when given."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor")
-    if t.dtype != dtype:
+    if t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {device}")
     return t
+
+
+def _shape(t, shape, name):
+    """Raise unless tensor t (skipped when None) has exactly `shape`: every
+    buffer the library writes or reads is sized from q's shape, so a mismatch
+    would be an out-of-bounds device access."""
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _qshape(q, name="q"):
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError(f"{name} must be a 4-D tensor [B, H, N, d]")
+    return tuple(q.shape)
+
+
+def _lists(idx, cnt, B, H, nb, name):
+    """A [B, H, nb, width] list and its [B, H, nb] counts."""
+    if idx is None or cnt is None:
+        raise ValueError(f"{name}_idx and {name}_cnt are both required")
+    if idx.dim() != 4 or tuple(idx.shape[:3]) != (B, H, nb) or idx.shape[3] < 1:
+        raise ValueError(f"{name}_idx must have shape ({B}, {H}, {nb}, width), got {tuple(idx.shape)}")
+    _shape(cnt, (B, H, nb), f"{name}_cnt")
 
 
 def num_blocks(N, block):
@@ -145,17 +177,33 @@ def counts_for(mode, nkb, keep=None, marg=None):
 # one wrapper per C entry point
 # ---------------------------------------------------------------------------
 
+def _pool_classify_args(q, k, block, q_pool, k_pool, cls):
+    B, H, N, d = _qshape(q)
+    nb = num_blocks(N, block)
+    _shape(k, q.shape, "k")
+    _shape(q_pool, (B, H, nb, d), "q_pool")
+    _shape(k_pool, (B, H, nb, d), "k_pool")
+    _shape(cls, (B, H, nb, nb), "cls")
+    _dev(q, torch.bfloat16, "q")
+    _dev(k, torch.bfloat16, "k", q.device)
+    for t, n in ((q_pool, "q_pool"), (k_pool, "k_pool")):
+        if t is not None:
+            _dev(t, torch.float32, n, q.device)
+    if cls is not None:
+        _dev(cls, torch.uint8, "cls", q.device)
+    return B, H, N, d, nb
+
+
 def sla_pool_classify(q, k, block, mode, k_crit=0, k_marg=0, thr=0.0, scale=None, q_pool=None,
                       k_pool=None, cls=None, ws=None, stream=None):
-    _dev(q, torch.bfloat16, "q")
-    _dev(k, torch.bfloat16, "k")
-    B, H, N, d = q.shape
-    nb = num_blocks(N, block)
+    B, H, N, d, nb = _pool_classify_args(q, k, block, q_pool, k_pool, cls)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if cls is None:
         cls = torch.empty((B, H, nb, nb), dtype=torch.uint8, device=q.device)
     need = lib().sla_pool_classify_ws_bytes(B, H, N, d, block, int(q_pool is not None))
+    if ws is not None:
+        _dev(ws, torch.uint8, "ws", q.device)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _call("sla_pool_classify", _ptr(q), _ptr(k), B, H, N, d, block, MODES.get(mode, mode),
@@ -169,10 +217,7 @@ def sla_pool_classify_noalloc(q, k, block, mode, k_crit=0, k_marg=0, thr=0.0, sc
     """sla_pool_classify without a workspace (the library's static device
     scratch instead): for callers that cannot allocate.  Pass `cls` (and the
     pooled outputs, if wanted) to make the whole call allocation-free."""
-    _dev(q, torch.bfloat16, "q")
-    _dev(k, torch.bfloat16, "k")
-    B, H, N, d = q.shape
-    nb = num_blocks(N, block)
+    B, H, N, d, nb = _pool_classify_args(q, k, block, q_pool, k_pool, cls)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if cls is None:
@@ -185,9 +230,22 @@ def sla_pool_classify_noalloc(q, k, block, mode, k_crit=0, k_marg=0, thr=0.0, sc
 
 def sla_block_mask(cls, kc_max, km_max=0, crit_idx=None, crit_cnt=None, marg_idx=None,
                    marg_cnt=None, err_flag=None, stream=None):
+    B, H, nqb, nkb = _qshape(cls, "cls")
+    if (crit_idx is None) != (crit_cnt is None) or (marg_idx is None) != (marg_cnt is None):
+        raise ValueError("give each list with its counts, or neither")
+    _shape(crit_idx, (B, H, nqb, kc_max), "crit_idx")
+    _shape(crit_cnt, (B, H, nqb), "crit_cnt")
+    if km_max:
+        _shape(marg_idx, (B, H, nqb, km_max), "marg_idx")
+        _shape(marg_cnt, (B, H, nqb), "marg_cnt")
+    if err_flag is not None and err_flag.numel() < 1:
+        raise ValueError("err_flag must hold one int32")
     _dev(cls, torch.uint8, "cls")
-    B, H, nqb, nkb = cls.shape
     dev = cls.device
+    for t, n in ((crit_idx, "crit_idx"), (crit_cnt, "crit_cnt"), (marg_idx, "marg_idx"),
+                 (marg_cnt, "marg_cnt"), (err_flag, "err_flag")):
+        if t is not None:
+            _dev(t, torch.int32, n, dev)
     if crit_idx is None:
         crit_idx = torch.empty((B, H, nqb, kc_max), dtype=torch.int32, device=dev)
         crit_cnt = torch.empty((B, H, nqb), dtype=torch.int32, device=dev)
@@ -199,13 +257,42 @@ def sla_block_mask(cls, kc_max, km_max=0, crit_idx=None, crit_cnt=None, marg_idx
     return crit_idx, crit_cnt, marg_idx, marg_cnt
 
 
+def _attn_args(q, k, v, block, lists=(), outs=(), lse=None):
+    """Shape and device checks shared by the attention wrappers: k and v (and
+    any extra [B, H, N, d] buffers in outs, given as (tensor, name, dtypes))
+    like q; each (idx, cnt, name) list of lists; lse [B, H, N]."""
+    B, H, N, d = _qshape(q)
+    nb = num_blocks(N, block)
+    for t, n in ((k, "k"), (v, "v")):
+        if t is not None:
+            _shape(t, q.shape, n)
+    for idx, cnt, n in lists:
+        _lists(idx, cnt, B, H, nb, n)
+    for t, n, _ in outs:
+        _shape(t, q.shape, n)
+    _shape(lse, (B, H, N), "lse")
+    _dev(q, torch.bfloat16, "q")
+    for t, n in ((k, "k"), (v, "v")):
+        if t is not None:
+            _dev(t, torch.bfloat16, n, q.device)
+    for idx, cnt, n in lists:
+        _dev(idx, torch.int32, f"{n}_idx", q.device)
+        _dev(cnt, torch.int32, f"{n}_cnt", q.device)
+    for t, n, dt in outs:
+        if t is not None:
+            _dev(t, dt, n, q.device)
+    if lse is not None:
+        _dev(lse, torch.float32, "lse", q.device)
+    return B, H, N, d, nb
+
+
+_O_TYPES = (torch.float32, torch.bfloat16)
+
+
 def sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, scale=None, o_s=None, o_fp32=True,
                         lse=None, want_lse=False, stream=None):
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, torch.bfloat16, n)
-    _dev(crit_idx, torch.int32, "crit_idx")
-    _dev(crit_cnt, torch.int32, "crit_cnt")
-    B, H, N, d = q.shape
+    B, H, N, d, _ = _attn_args(q, k, v, block, [(crit_idx, crit_cnt, "crit")],
+                               [(o_s, "o_s", _O_TYPES)], lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if o_s is None:
@@ -220,9 +307,7 @@ def sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, scale=None, o_s=None
 
 def sla_dense_attn_fwd(q, k, v, block, scale=None, o=None, o_fp32=False, lse=None, want_lse=False,
                        stream=None):
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, torch.bfloat16, n)
-    B, H, N, d = q.shape
+    B, H, N, d, _ = _attn_args(q, k, v, block, [], [(o, "o", _O_TYPES)], lse)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if o is None:
@@ -235,11 +320,10 @@ def sla_dense_attn_fwd(q, k, v, block, scale=None, o=None, o_fp32=False, lse=Non
 
 
 def sla_linear_branch_fwd(q, k, v, block, marg_idx, marg_cnt, o_lin=None, ws=None, stream=None):
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, torch.bfloat16, n)
-    _dev(marg_idx, torch.int32, "marg_idx")
-    _dev(marg_cnt, torch.int32, "marg_cnt")
-    B, H, N, d = q.shape
+    B, H, N, d, _ = _attn_args(q, k, v, block, [(marg_idx, marg_cnt, "marg")],
+                               [(o_lin, "o_lin", torch.float32)])
+    if ws is not None:
+        _dev(ws, torch.uint8, "ws", q.device)
     if o_lin is None:
         o_lin = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     need = lib().sla_linear_branch_ws_bytes(B, H, N, d, block)
@@ -252,11 +336,9 @@ def sla_linear_branch_fwd(q, k, v, block, marg_idx, marg_cnt, o_lin=None, ws=Non
 
 
 def sla_linear_branch_prepare(k, v, block, marg_idx, marg_cnt, ws=None, stream=None):
-    for t, n in ((k, "k"), (v, "v")):
-        _dev(t, torch.bfloat16, n)
-    _dev(marg_idx, torch.int32, "marg_idx")
-    _dev(marg_cnt, torch.int32, "marg_cnt")
-    B, H, N, d = k.shape
+    B, H, N, d, _ = _attn_args(k, v, None, block, [(marg_idx, marg_cnt, "marg")])
+    if ws is not None:
+        _dev(ws, torch.uint8, "ws", k.device)
     need = lib().sla_linear_branch_ws_bytes(B, H, N, d, block)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=k.device)
@@ -268,12 +350,9 @@ def sla_linear_branch_prepare(k, v, block, marg_idx, marg_cnt, ws=None, stream=N
 
 def sla_sparse_linear_attn_fwd(q, k, v, block, crit_idx, crit_cnt, lin_ws, scale=None, o=None,
                                o_fp32=False, lse=None, want_lse=False, stream=None):
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _dev(t, torch.bfloat16, n)
-    _dev(crit_idx, torch.int32, "crit_idx")
-    _dev(crit_cnt, torch.int32, "crit_cnt")
-    _dev(lin_ws, torch.uint8, "lin_ws")
-    B, H, N, d = q.shape
+    B, H, N, d, _ = _attn_args(q, k, v, block, [(crit_idx, crit_cnt, "crit")],
+                               [(o, "o", _O_TYPES)], lse)
+    _dev(lin_ws, torch.uint8, "lin_ws", q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if o is None:
@@ -288,12 +367,14 @@ def sla_sparse_linear_attn_fwd(q, k, v, block, crit_idx, crit_cnt, lin_ws, scale
 
 def sla_sparse_attn_bwd(q, k, v, block, crit_idx, crit_cnt, o_s, lse, d_o, scale=None, dq=None,
                         dk=None, dv=None, ws=None, stream=None):
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
-        _dev(t, torch.bfloat16, n)
-    _dev(crit_idx, torch.int32, "crit_idx")
-    _dev(crit_cnt, torch.int32, "crit_cnt")
-    _dev(lse, torch.float32, "lse")
-    B, H, N, d = q.shape
+    if o_s is None or lse is None or d_o is None:
+        raise ValueError("o_s, lse and d_o are required")
+    B, H, N, d, _ = _attn_args(q, k, v, block, [(crit_idx, crit_cnt, "crit")],
+                               [(o_s, "o_s", _O_TYPES), (d_o, "d_o", torch.bfloat16),
+                                (dq, "dq", torch.float32), (dk, "dk", torch.float32),
+                                (dv, "dv", torch.float32)], lse)
+    if ws is not None:
+        _dev(ws, torch.uint8, "ws", q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) if t is None else t
@@ -311,14 +392,14 @@ def sla_sparse_attn_bwd(q, k, v, block, crit_idx, crit_cnt, o_s, lse, d_o, scale
 def sla_linear_branch_bwd(q, k, v, block, marg_idx, marg_cnt, d_o, lin_ws, dq, dk, dv, ws=None,
                           stream=None):
     """Adds the linear branch's gradients into dq, dk, dv (fp32)."""
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (d_o, "d_o")):
-        _dev(t, torch.bfloat16, n)
-    _dev(marg_idx, torch.int32, "marg_idx")
-    _dev(marg_cnt, torch.int32, "marg_cnt")
-    _dev(lin_ws, torch.uint8, "lin_ws")
-    for t, n in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _dev(t, torch.float32, n)
-    B, H, N, d = q.shape
+    if d_o is None or dq is None or dk is None or dv is None:
+        raise ValueError("d_o, dq, dk and dv are required")
+    B, H, N, d, _ = _attn_args(q, k, v, block, [(marg_idx, marg_cnt, "marg")],
+                               [(d_o, "d_o", torch.bfloat16), (dq, "dq", torch.float32),
+                                (dk, "dk", torch.float32), (dv, "dv", torch.float32)])
+    _dev(lin_ws, torch.uint8, "lin_ws", q.device)
+    if ws is not None:
+        _dev(ws, torch.uint8, "ws", q.device)
     need = lib().sla_linear_branch_bwd_ws_bytes(B, H, N, d, block)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
@@ -331,11 +412,9 @@ def sla_linear_branch_bwd(q, k, v, block, marg_idx, marg_cnt, d_o, lin_ws, dq, d
 def sla_mask_recall(q, k, block, crit_idx, crit_cnt, scale=None, recall=None, ws=None,
                     stream=None):
     """Share of each query's dense softmax mass held by its kept tiles, fp32 [B, H, N]."""
-    _dev(q, torch.bfloat16, "q")
-    _dev(k, torch.bfloat16, "k")
-    _dev(crit_idx, torch.int32, "crit_idx")
-    _dev(crit_cnt, torch.int32, "crit_cnt")
-    B, H, N, d = q.shape
+    B, H, N, d, _ = _attn_args(q, k, None, block, [(crit_idx, crit_cnt, "crit")], [], recall)
+    if ws is not None:
+        _dev(ws, torch.uint8, "ws", q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if recall is None:
@@ -353,8 +432,11 @@ def sla_tile_permute(x, grid, tiles, block, inverse=False, y=None, stream=None):
     """Rows of x [B, H, T*Y*X, d] into per-head 3D tile order (or back, inverse=True).
 
     grid = (T, Y, X); tiles = one (bt, by, bx) per head (host ints)."""
+    B, H, N, d = _qshape(x, "x")
+    _shape(y, x.shape, "y")
     _dev(x, torch.bfloat16, "x")
-    B, H, N, d = x.shape
+    if y is not None:
+        _dev(y, torch.bfloat16, "y", x.device)
     T, Y, X = (int(g) for g in grid)
     if len(tiles) != H:
         raise ValueError(f"need one tile shape per head ({H}), got {len(tiles)}")
@@ -367,11 +449,44 @@ def sla_tile_permute(x, grid, tiles, block, inverse=False, y=None, stream=None):
 
 
 def sla_combine(o_s, o_lin=None, o=None, stream=None):
+    if not isinstance(o_s, torch.Tensor):
+        raise ValueError("o_s must be a tensor")
+    _shape(o_lin, o_s.shape, "o_lin")
+    _shape(o, o_s.shape, "o")
+    _dev(o_s, _O_TYPES, "o_s")
+    if o_lin is not None:
+        _dev(o_lin, torch.float32, "o_lin", o_s.device)
+    if o is not None:
+        _dev(o, torch.bfloat16, "o", o_s.device)
     if o is None:
         o = torch.empty(o_s.shape, dtype=torch.bfloat16, device=o_s.device)
     _call("sla_combine", _ptr(o_s), int(o_s.dtype == torch.float32), _ptr(o_lin), _ptr(o),
           o_s.numel(), _stream(stream))
     return o
+
+
+def sla_check_lists(idx, cnt, nkb, err_flag=None, stream=None):
+    """OR the FLAG_LIST_* bits of every violation of the list form (entries in
+    [0, nkb), strictly ascending, counts in [0, width]) into err_flag (device
+    int32 [1], zeroed here when not given); returns err_flag."""
+    if not isinstance(idx, torch.Tensor) or idx.dim() < 1:
+        raise ValueError("idx must be a tensor [..., width]")
+    _shape(cnt, idx.shape[:-1], "cnt")
+    _dev(idx, torch.int32, "idx")
+    _dev(cnt, torch.int32, "cnt", idx.device)
+    if err_flag is None:
+        err_flag = torch.zeros(1, dtype=torch.int32, device=idx.device)
+    _dev(err_flag, torch.int32, "err_flag", idx.device)
+    rows = idx.numel() // idx.shape[-1]
+    _call("sla_check_lists", _ptr(idx), _ptr(cnt), rows, idx.shape[-1], int(nkb), _ptr(err_flag),
+          _stream(stream))
+    return err_flag
+
+
+def debug_flag_address():
+    """Device address of the debug flag word (library built with
+    SLA_DEBUG_CHECKS), or None for the release build."""
+    return lib().sla_debug_flag()
 
 
 # ---------------------------------------------------------------------------
@@ -388,12 +503,22 @@ def _select(q, k, block, mode, keep, marg, thr, cls, stream):
         cls = sla_pool_classify(q, k, block, mode, kc, km, thr or 0.0, stream=stream)
         kc_max = nb if mode == "cdf" else kc
         km_max = km
-    else:
-        # a given map: the fractions, when given, only size the lists
-        kc_max = count_from_fraction(keep, nb) if keep is not None else nb
-        km_max = (counts_for("sla3", nb, keep, marg)[1] if keep is not None and marg is not None
-                  else nb)
-    crit_idx, crit_cnt, marg_idx, marg_cnt = sla_block_mask(cls, kc_max, km_max, stream=stream)
+        crit_idx, crit_cnt, marg_idx, marg_cnt = sla_block_mask(cls, kc_max, km_max, stream=stream)
+        return cls, crit_idx, crit_cnt, marg_idx, marg_cnt
+    # a given map: the fractions, when given, only size the lists, and a row
+    # with more tiles than that width (which sla_block_mask would cut) raises
+    kc_max = count_from_fraction(keep, nb) if keep is not None else nb
+    km_max = (counts_for("sla3", nb, keep, marg)[1] if keep is not None and marg is not None
+              else nb)
+    flag = torch.zeros(1, dtype=torch.int32, device=q.device)
+    crit_idx, crit_cnt, marg_idx, marg_cnt = sla_block_mask(cls, kc_max, km_max, err_flag=flag,
+                                                            stream=stream)
+    bits = int(flag.item())
+    if bits & FLAG_OVERFLOW:
+        raise ValueError(f"the given class map has a row with more critical or marginal tiles "
+                         f"than the list widths ({kc_max}, {km_max}) that keep/marg imply")
+    if bits & FLAG_BAD_CLASS:
+        raise ValueError("the given class map holds a class value above 2")
     return cls, crit_idx, crit_cnt, marg_idx, marg_cnt
 
 

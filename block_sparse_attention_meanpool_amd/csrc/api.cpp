@@ -84,9 +84,50 @@ sla_status run_pool_classify(const uint16_t* q, const uint16_t* k, int64_t BH, i
   return from_hip(sla::launch_select(S, cls, BH * nb, (int)nb, mode, kc, km, thr, stream));
 }
 
+// Builds with SLA_DEBUG_CHECKS validate every list argument before the call
+// that reads it, into the library's per-device debug flag (sla_debug_flag).
+#ifdef SLA_DEBUG_CHECKS
+sla_status debug_check_lists(const int32_t* idx, const int32_t* cnt, int64_t rows, int width,
+                             int64_t nkb, hipStream_t stream) {
+  int32_t* flag = nullptr;
+  sla_status st = from_hip(sla::debug_flag_ptr(&flag));
+  if (st != SLA_OK) return st;
+  return from_hip(sla::launch_check_lists(idx, cnt, rows, width, (int)nkb, flag, stream));
+}
+#define SLA_DEBUG_LISTS(idx, cnt, rows, width, nkb, stream)                         \
+  do {                                                                              \
+    const sla_status dbg_ = debug_check_lists(idx, cnt, rows, width, nkb, stream); \
+    if (dbg_ != SLA_OK) return dbg_;                                                \
+  } while (0)
+#else
+#define SLA_DEBUG_LISTS(idx, cnt, rows, width, nkb, stream) \
+  do {                                                      \
+  } while (0)
+#endif
+
 }  // namespace
 
 extern "C" {
+
+sla_status sla_check_lists(const int32_t* idx, const int32_t* cnt, int64_t rows, int32_t width,
+                           int64_t nkb, int32_t* err_flag, hipStream_t stream) {
+  if (!idx || !cnt || !err_flag) return SLA_ERR_INVALID_ARG;
+  if (rows < 1 || width < 1 || nkb < 1 || nkb > kMaxBlocks) return SLA_ERR_INVALID_ARG;
+  if ((rows + 3) / 4 > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
+  if (reinterpret_cast<uintptr_t>(idx) & 3u || reinterpret_cast<uintptr_t>(cnt) & 3u ||
+      reinterpret_cast<uintptr_t>(err_flag) & 3u)
+    return SLA_ERR_ALIGNMENT;
+  return from_hip(sla::launch_check_lists(idx, cnt, rows, width, (int)nkb, err_flag, stream));
+}
+
+int32_t* sla_debug_flag(void) {
+#ifdef SLA_DEBUG_CHECKS
+  int32_t* flag = nullptr;
+  return sla::debug_flag_ptr(&flag) == hipSuccess ? flag : nullptr;
+#else
+  return nullptr;
+#endif
+}
 
 size_t sla_pool_classify_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block,
                                   int32_t pooled_given) {
@@ -174,6 +215,7 @@ sla_status sla_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
   if (kc_max < 1 || kc_max > nb) return SLA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_s)) return SLA_ERR_ALIGNMENT;
+  SLA_DEBUG_LISTS(crit_idx, crit_cnt, B * H * nb, kc_max, nb, stream);
   return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
                                    crit_cnt, kc_max, scale, o_s, o_is_fp32 != 0, lse, nullptr,
                                    stream));
@@ -210,6 +252,7 @@ sla_status sla_linear_branch_prepare(const uint16_t* k, const uint16_t* v, int64
   if (!aligned16(k) || !aligned16(v)) return SLA_ERR_ALIGNMENT;
   const size_t need = sla_linear_branch_ws_bytes(B, H, N, d, block);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  SLA_DEBUG_LISTS(marg_idx, marg_cnt, B * H * nb, km_max, nb, stream);
   return from_hip(sla::launch_linear_prepare(k, v, B * H, (int)N, (int)d, block, (int)nb, marg_idx,
                                              marg_cnt, km_max, ws, stream));
 }
@@ -226,6 +269,7 @@ sla_status sla_linear_branch_fwd(const uint16_t* q, const uint16_t* k, const uin
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_lin)) return SLA_ERR_ALIGNMENT;
   const size_t need = sla_linear_branch_ws_bytes(B, H, N, d, block);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  SLA_DEBUG_LISTS(marg_idx, marg_cnt, B * H * nb, km_max, nb, stream);
   st = from_hip(sla::launch_linear_prepare(k, v, B * H, (int)N, (int)d, block, (int)nb, marg_idx,
                                            marg_cnt, km_max, ws, stream));
   if (st != SLA_OK) return st;
@@ -248,6 +292,7 @@ sla_status sla_sparse_linear_attn_fwd(const uint16_t* q, const uint16_t* k, cons
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SLA_ERR_ALIGNMENT;
   const size_t need = sla_linear_branch_ws_bytes(B, H, N, d, block);
   if (!lin_ws || lin_ws_bytes < need || !aligned16(lin_ws)) return SLA_ERR_WORKSPACE;
+  SLA_DEBUG_LISTS(crit_idx, crit_cnt, B * H * nb, kc_max, nb, stream);
   return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
                                    crit_cnt, kc_max, scale, o, o_is_fp32 != 0, lse, lin_ws,
                                    stream));
@@ -279,6 +324,7 @@ sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
   if ((BH * nb * kc_max + 255) / 256 > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
   const size_t need = sla_sparse_attn_bwd_ws_bytes(B, H, N, d, block);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  SLA_DEBUG_LISTS(crit_idx, crit_cnt, BH * nb, kc_max, nb, stream);
   return from_hip(sla::launch_attn_bwd(q, k, v, BH, (int)N, (int)d, block, (int)nb, crit_idx,
                                        crit_cnt, kc_max, scale, o_s, o_s_is_fp32 != 0, lse, d_o,
                                        dq, dk, dv, ws, stream));
@@ -312,6 +358,7 @@ sla_status sla_linear_branch_bwd(const uint16_t* q, const uint16_t* k, const uin
     return SLA_ERR_WORKSPACE;
   const size_t need = sla_linear_branch_bwd_ws_bytes(B, H, N, d, block);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  SLA_DEBUG_LISTS(marg_idx, marg_cnt, BH * nb, km_max, nb, stream);
   return from_hip(sla::launch_linear_bwd(q, k, v, BH, (int)N, (int)d, block, (int)nb, marg_idx,
                                          marg_cnt, km_max, d_o, lin_ws, dq, dk, dv, ws, stream));
 }
@@ -337,6 +384,7 @@ sla_status sla_mask_recall(const uint16_t* q, const uint16_t* k, int64_t B, int6
   if ((B * H * N + 255) / 256 > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
   const size_t need = sla_mask_recall_ws_bytes(B, H, N, d, block);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
+  SLA_DEBUG_LISTS(crit_idx, crit_cnt, B * H * nb, kc_max, nb, stream);
   return from_hip(sla::launch_recall(q, k, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
                                      crit_cnt, kc_max, scale, recall, ws, stream));
 }

@@ -234,8 +234,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 
   f32x16 dqacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   const int krow = swap_bits_2_3(l32);
+  const bool canon = __builtin_amdgcn_readfirstlane(list_is_canonical(list, count, nkb, lane));
   for (int t = 0; t < count; ++t) {
-    const bool ok = j_cur >= 0 && j_cur < nkb;
+    const bool ok = list_entry_used(list, t, j_cur, nkb, canon);  // the list is a set of tiles
     const int j_next = (t + 1 < count) ? list[t + 1] : 0;
     wait_vmcnt0();
     __syncthreads();  // buffer 0 complete; every wave is done with buffer 1

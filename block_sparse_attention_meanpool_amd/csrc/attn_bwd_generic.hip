@@ -107,6 +107,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(
 
   const int count = min(cnt[bh * nqb + qb], kmax);
   const int32_t* list = idx + (bh * nqb + qb) * (int64_t)kmax;
+  const bool canon = __builtin_amdgcn_readfirstlane(list_is_canonical(list, count, nkb, lane));
   f32x16 dqacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dqacc[db] = f32x16{};
@@ -114,8 +115,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(
 
   for (int t = 0; t < count; ++t) {
     const int j = list[t];
-    if (j < 0 || j >= nkb) continue;  // entries outside the key-block range are ignored
-    __syncthreads();                  // the previous tile's LDS reads are done
+    if (!list_entry_used(list, t, j, nkb, canon)) continue;  // the list is a set of tiles
+    __syncthreads();  // the previous tile's LDS reads are done
     stage<D, BLK>(rk, j * BLK, Ks, Kt, tid);
     stage<D, BLK>(rv, j * BLK, Vs, nullptr, tid);
     __syncthreads();

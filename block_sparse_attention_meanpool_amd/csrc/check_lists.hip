@@ -1,0 +1,82 @@
+// Validation of per-query-block tile lists supplied by a caller (the lists
+// the block-mask kernel writes always pass): every entry in [0, nkb), no
+// repeated entry, ascending order, and a count in [0, width].  The kernels
+// that read lists treat a list as a set of tiles whatever it holds; this check
+// tells a caller that its lists were not in the documented form.
+#include <hip/hip_runtime.h>
+
+#include <mutex>
+
+#include "../../include/sla.h"
+#include "launch.h"
+
+namespace sla {
+
+// One wave per row.  A per-wave bitmap in LDS (nkb <= 4096 bits) finds
+// repeated entries in any order; neighbouring entries give the order check.
+__global__ __launch_bounds__(256) void check_lists_kernel(const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ cnt,
+                                                          int64_t rows, int width, int nkb,
+                                                          int32_t* __restrict__ err_flag) {
+  __shared__ uint32_t seen[4][128];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t row = (int64_t)blockIdx.x * 4 + wv;
+  if (row >= rows) return;
+  seen[wv][lane] = 0u;
+  seen[wv][lane + 64] = 0u;
+  __builtin_amdgcn_wave_barrier();
+  int flags = 0;
+  const int c0 = cnt[row];
+  if (c0 < 0 || c0 > width) flags |= SLA_FLAG_LIST_COUNT;
+  const int c = min(max(c0, 0), width);
+  const int32_t* list = idx + row * (int64_t)width;
+  for (int t0 = 0; t0 < c; t0 += 64) {
+    const int t = t0 + lane;
+    if (t < c) {
+      const int j = list[t];
+      if (j < 0 || j >= nkb) {
+        flags |= SLA_FLAG_LIST_RANGE;
+      } else {
+        const uint32_t bit = 1u << (j & 31);
+        if (atomicOr(&seen[wv][j >> 5], bit) & bit) flags |= SLA_FLAG_LIST_REPEAT;
+      }
+      if (t + 1 < c && list[t + 1] < j) flags |= SLA_FLAG_LIST_ORDER;
+    }
+  }
+  if (flags) atomicOr(err_flag, flags);
+}
+
+hipError_t launch_check_lists(const int32_t* idx, const int32_t* cnt, int64_t rows, int width,
+                              int nkb, int32_t* err_flag, hipStream_t s) {
+  check_lists_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(idx, cnt, rows, width, nkb,
+                                                                     err_flag);
+  return hipGetLastError();
+}
+
+// The flag word that builds with SLA_DEBUG_CHECKS report list violations in
+// (each device holds its own), addressed through hipGetSymbolAddress as for
+// any device symbol: the name itself is a host-side stand-in.
+static __device__ int32_t debug_flag;
+
+namespace {
+std::mutex g_dbg_mu;
+void* g_dbg_ptr[64] = {};
+}  // namespace
+
+hipError_t debug_flag_ptr(int32_t** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_dbg_mu);
+  if (!g_dbg_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(debug_flag));
+    if (e != hipSuccess) return e;
+    g_dbg_ptr[dev] = p;
+  }
+  *ptr = static_cast<int32_t*>(g_dbg_ptr[dev]);
+  return hipSuccess;
+}
+
+}  // namespace sla

@@ -132,6 +132,13 @@ hipError_t launch_tile_permute(const uint16_t* x, uint16_t* y, int64_t BH, int H
                                int X, int d, const TileShapes& ts, int inverse, hipStream_t s);
 hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,
                           int64_t n_elems, hipStream_t s);
+// ORs SLA_FLAG_LIST_* bits into *err_flag for rows of `width`-wide lists
+// whose first cnt entries leave [0, nkb), repeat, descend, or whose count
+// lies outside [0, width]
+hipError_t launch_check_lists(const int32_t* idx, const int32_t* cnt, int64_t rows, int width,
+                              int nkb, int32_t* err_flag, hipStream_t s);
+// Device address of the debug flag word on the current device
+hipError_t debug_flag_ptr(int32_t** ptr);
 // Bytes of the static device scratch behind sla_pool_classify_noalloc: one
 // head's pooled Q and K and fp32 scores at the largest block count (4096
 // blocks, d = 128) fit, so every supported shape runs, a chunk of heads at a

@@ -20,6 +20,7 @@
 #include "common.h"
 #include "launch.h"
 #include "linear_apply.h"
+#include "lists.h"
 
 namespace sla {
 
@@ -64,6 +65,8 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(D == 64
 
   const int count = LIST ? min(cnt[bh * nqb + qb], kmax) : nkb;
   const int32_t* list = LIST ? idx + (bh * nqb + qb) * (int64_t)kmax : nullptr;
+  const bool canon =
+      LIST ? __builtin_amdgcn_readfirstlane(list_is_canonical(list, count, nkb, lane)) : true;
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(D == 64
 
   for (int t = 0; t < count; ++t) {
     const int j = LIST ? list[t] : t;
-    if (j < 0 || j >= nkb) continue;  // ignore entries outside the key-block range
+    if (LIST && !list_entry_used(list, t, j, nkb, canon)) continue;  // the list is a set of tiles
     __syncthreads();  // previous tile's LDS reads are done
     // K tile, row-major, swizzled chunks.
     {
@@ -363,9 +366,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   f32x16 oacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   float m_run = -INFINITY, l_run = 0.f;
   const int krow = swap_bits_2_3(l32);
+  // the list is a set of tiles: checked once, after the first loads are issued
+  const bool canon =
+      LIST ? __builtin_amdgcn_readfirstlane(list_is_canonical(list, count, nkb, lane)) : true;
 
   for (int t = 0; t < count; ++t) {
-    const bool ok = j_cur >= 0 && j_cur < nkb;
+    const bool ok = LIST ? list_entry_used(list, t, j_cur, nkb, canon) : true;
     // next tile index: loaded before the wait below, which drains it together
     // with the loads of buffer 0
     const int j_next = (t + 1 < count) ? (LIST ? list[t + 1] : t + 1) : 0;

@@ -65,6 +65,22 @@ typedef int32_t sla_status;
 /* Bits set in the device error flag of sla_block_mask. */
 #define SLA_FLAG_BAD_CLASS 1 /* a class value > 2 was found (treated as skipped)   */
 #define SLA_FLAG_OVERFLOW  2 /* a row held more blocks than its list width         */
+/* Bits set by sla_check_lists (and by builds with SLA_DEBUG_CHECKS). */
+#define SLA_FLAG_LIST_RANGE  4  /* an entry outside [0, nkb)                       */
+#define SLA_FLAG_LIST_REPEAT 8  /* an entry equal to an earlier one of its row     */
+#define SLA_FLAG_LIST_ORDER  16 /* an entry smaller than the one before it         */
+#define SLA_FLAG_LIST_COUNT  32 /* a count outside [0, width]                      */
+
+/*
+ * Tile lists (crit_idx/crit_cnt, marg_idx/marg_cnt) are read as SETS of key
+ * tiles by every call that takes them: the first min(count, width) entries of
+ * a row are read; an entry outside [0, nkb) is ignored, and an entry equal to
+ * an earlier one of its row is ignored (the tile is used once, at its first
+ * position).  sla_block_mask writes strictly ascending lists, which need none
+ * of this; the softmax branch visits a row's tiles in list order, so a list
+ * in another order gives the same set with a different (equally valid)
+ * summation order.
+ */
 
 /*
  * Mean-pool Q and K over blocks, score every (query block, key block) pair
@@ -156,7 +172,7 @@ sla_status sla_block_mask(const uint8_t* cls, int64_t B, int64_t H, int64_t nqb,
  * A row with crit_cnt = 0 gets O_s = 0 and LSE = -inf.  bf16 MFMA products,
  * fp32 online softmax and accumulation.
  *
- * crit_idx/crit_cnt  as written by sla_block_mask; every index in [0, nb)
+ * crit_idx/crit_cnt  as written by sla_block_mask (read as sets, see above)
  * o_s       [B, H, N, d]; fp32 when o_is_fp32 != 0, else bf16 (RNE) (out)
  * lse       fp32 [B, H, N] or NULL                              (out)
  */
@@ -248,8 +264,8 @@ sla_status sla_combine(const void* o_s, int32_t o_s_is_fp32, const float* o_lin,
  * each key and value summing over every query block whose list holds its tile.
  * bf16 MFMA products (P and dS rounded to bf16), fp32 accumulation.
  *
- * q, k, v, crit_idx, crit_cnt, kc_max, scale  as given to sla_sparse_attn_fwd;
- *           the lists must hold no repeated entry (sla_block_mask writes none)
+ * q, k, v, crit_idx, crit_cnt, kc_max, scale  as given to sla_sparse_attn_fwd
+ *           (the lists read as sets, as there)
  * o_s, lse  that call's outputs (o_s fp32 when o_s_is_fp32 != 0, else bf16)
  * d_o       bf16 [B, H, N, d]                                   (in)
  * dq, dk, dv  fp32 [B, H, N, d], overwritten                    (out)
@@ -351,6 +367,29 @@ sla_status sla_tile_permute(const uint16_t* x, uint16_t* y, int64_t B, int64_t H
 sla_status sla_dense_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                               int64_t H, int64_t N, int64_t d, int32_t block, float scale, void* o,
                               int32_t o_is_fp32, float* lse, hipStream_t stream);
+
+/*
+ * Validate tile lists supplied by a caller (the Veda article's per-query sets
+ * of key tiles; the form sla_block_mask writes): for each of `rows` rows of
+ * `width` entries, the first cnt entries must lie in [0, nkb), be strictly
+ * ascending and so hold no repeat, and cnt must lie in [0, width].  Each
+ * violation ORs its SLA_FLAG_LIST_* bit into *err_flag (device int32, never
+ * cleared by the library).  Lists that fail still have a defined meaning (the
+ * set rule above); the check tells the caller they were not canonical.
+ *
+ * idx   int32 [rows, width] (in);  cnt  int32 [rows] (in)
+ */
+sla_status sla_check_lists(const int32_t* idx, const int32_t* cnt, int64_t rows, int32_t width,
+                           int64_t nkb, int32_t* err_flag, hipStream_t stream);
+
+/*
+ * Builds compiled with SLA_DEBUG_CHECKS validate every list argument as
+ * sla_check_lists does, before each call that reads lists, into a flag word
+ * the library keeps on each device; this returns that word's device address
+ * on the current device (read it and clear it with ordinary copies).  NULL in
+ * builds without SLA_DEBUG_CHECKS.
+ */
+int32_t* sla_debug_flag(void);
 
 /* Human-readable text for a status code (static storage). */
 const char* sla_status_string(sla_status status);

@@ -22,7 +22,7 @@ pytestmark = pytest.mark.skipif(
 
 def _declared():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:sla_status|size_t|const char\*|int32_t)\s+(sla_\w+)\(",
+    return sorted(set(re.findall(r"^\s*(?:sla_status|size_t|const char\*|int32_t\*?)\s+(sla_\w+)\(",
                                  text, flags=re.M)))
 
 
@@ -188,3 +188,88 @@ def test_counts_match_the_fraction_reading(mod):
     assert mod.counts_for("sla3", 256, F(5, 100), F(15, 100)) == (13, 39)
     assert mod.counts_for("sla3", 1920, F(10, 100), F(5, 100)) == (192, 96)
     assert mod.counts_for("cdf", 128) == (0, 0)
+
+
+def test_list_validation_and_debug_flag_reject_bad_arguments(mod):
+    lib = mod.lib()
+    cl = lib.sla_check_lists
+    assert cl(None, GOOD, 4, 2, 8, GOOD, None) == -1
+    assert cl(GOOD, GOOD, 4, 2, 8, None, None) == -1
+    assert cl(GOOD, GOOD, 0, 2, 8, GOOD, None) == -1
+    assert cl(GOOD, GOOD, 4, 2, 4097, GOOD, None) == -1
+    assert cl(GOOD, P(0x10002), 4, 2, 8, GOOD, None) == -3
+    # the release build keeps no debug flag
+    if os.path.abspath(mod.LIB_PATH) == os.path.join(ROOT, "block_sparse_attention_meanpool_amd",
+                                                     "libsla.so"):
+        assert mod.debug_flag_address() is None
+
+
+def test_noalloc_entry_point_rejects_bad_arguments(mod):
+    lib = mod.lib()
+    assert lib.sla_pool_classify_noalloc_scratch_bytes() == 80 << 20
+
+    def call(q=GOOD, d=64, kc=4, mode=0, scale=0.125):
+        return lib.sla_pool_classify_noalloc(q, GOOD, 1, 2, 1024, d, 64, mode, kc, 0, 0.0, scale,
+                                             None, None, GOOD, None)
+    assert call(q=None) == -1
+    assert call(d=96) == -2
+    assert call(q=ODD) == -3
+    assert call(kc=0) == -1
+    assert call(mode=9) == -1
+    assert call(scale=0.0) == -1
+
+
+def test_wrappers_reject_mismatched_shapes_before_any_device_use(mod):
+    """Every buffer the library touches is sized from q's shape: the wrappers
+    compare each given tensor's shape with it before anything else (these are
+    CPU tensors, so a call that passed the shape checks would stop at the
+    device check instead)."""
+    import torch
+    B, H, N, d, b = 1, 2, 300, 64, 64
+    nb = 5
+    bf = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)
+    i32 = lambda *s: torch.zeros(s, dtype=torch.int32)
+    q, k, v = bf(B, H, N, d), bf(B, H, N, d), bf(B, H, N, d)
+    ci, cc = i32(B, H, nb, 2), i32(B, H, nb)
+    cases = [
+        lambda: mod.sla_pool_classify(q, bf(B, H, N + 1, d), b, "topk", 1),
+        lambda: mod.sla_pool_classify(q, k, b, "topk", 1, cls=torch.zeros((B, H, nb, nb + 1),
+                                                                          dtype=torch.uint8)),
+        lambda: mod.sla_pool_classify(q, k, b, "topk", 1, q_pool=f32(B, H, nb, d - 1),
+                                      k_pool=f32(B, H, nb, d)),
+        lambda: mod.sla_pool_classify_noalloc(q, k, b, "topk", 1, cls=torch.zeros((B, H, nb, 4),
+                                                                                  dtype=torch.uint8)),
+        lambda: mod.sla_block_mask(torch.zeros((B, H, nb, nb), dtype=torch.uint8), 2,
+                                   crit_idx=i32(B, H, nb, 3), crit_cnt=cc),
+        lambda: mod.sla_block_mask(torch.zeros((B, H, nb, nb), dtype=torch.uint8), 2, 2,
+                                   crit_idx=ci, crit_cnt=cc, marg_idx=i32(B, H, nb, 2),
+                                   marg_cnt=i32(B, H, nb - 1)),
+        lambda: mod.sla_sparse_attn_fwd(q, k, bf(B, H, N, d + 1), b, ci, cc),
+        lambda: mod.sla_sparse_attn_fwd(q, k, v, b, i32(B, H, nb + 1, 2), cc),
+        lambda: mod.sla_sparse_attn_fwd(q, k, v, b, ci, i32(B, H, nb + 1)),
+        lambda: mod.sla_sparse_attn_fwd(q, k, v, b, ci, cc, o_s=f32(B, H, N - 1, d)),
+        lambda: mod.sla_sparse_attn_fwd(q, k, v, b, ci, cc, lse=f32(B, H, N + 1)),
+        lambda: mod.sla_dense_attn_fwd(q, k, v, b, o=bf(B, H + 1, N, d)),
+        lambda: mod.sla_linear_branch_fwd(q, k, v, b, ci, cc, o_lin=f32(B, H, N, 2 * d)),
+        lambda: mod.sla_linear_branch_prepare(k, bf(B, H, N, 2 * d), b, ci, cc),
+        lambda: mod.sla_sparse_linear_attn_fwd(q, k, v, b, ci, i32(B, H), torch.zeros(16, dtype=torch.uint8)),
+        lambda: mod.sla_sparse_attn_bwd(q, k, v, b, ci, cc, f32(B, H, N, d), f32(B, H, N),
+                                        bf(B, H, N - 2, d)),
+        lambda: mod.sla_sparse_attn_bwd(q, k, v, b, ci, cc, f32(B, H, N, d), f32(B, H, N),
+                                        bf(B, H, N, d), dk=f32(B, H, N, d + 2)),
+        lambda: mod.sla_linear_branch_bwd(q, k, v, b, ci, cc, bf(B, H, N, d),
+                                          torch.zeros(16, dtype=torch.uint8), f32(B, H, N, d),
+                                          f32(B, H, N, d), f32(B, H, N + 1, d)),
+        lambda: mod.sla_mask_recall(q, k, b, ci, cc, recall=f32(B, H, N, 1)),
+        lambda: mod.sla_tile_permute(q, (3, 10, 10), [(1, 8, 8)] * H, b, y=bf(B, H, N, d + 8)),
+        lambda: mod.sla_combine(f32(B, H, N, d), f32(B, H, N, d + 8)),
+        lambda: mod.sla_check_lists(ci, i32(B, H, nb + 1), nb),
+    ]
+    for i, case in enumerate(cases):
+        with pytest.raises(ValueError, match="shape") as e:
+            case()
+        assert "shape" in str(e.value), i
+    # with consistent shapes the same CPU tensors stop at the device check
+    with pytest.raises(ValueError, match="GPU tensor"):
+        mod.sla_sparse_attn_fwd(q, k, v, b, ci, cc)
