@@ -1,15 +1,18 @@
 """GPU parity on the five workloads at their full sizes, through the C ABI.
 
 Block masks (class map and lists) are compared bit-exactly in full.  Outputs
-are compared on every query block for the two small workloads and on a
-seeded sample of query blocks (always including the first and the last,
-possibly ragged, block of each head) for the large ones, using the same
-launches the benchmark times.  For the long-clip layer the mask is given as
-input (the oracle's per-head top-k plus the next 5% as marginal), and the
-GPU classifier is checked against it as well.
+are compared, on the launches the benchmark times:
+  * tiny, short video, the 32k-token layer and the 75k-token layer: every
+    query block of every head;
+  * the long-clip layer (95% and 90%): every query block of two whole heads
+    (0 and 23), and the first, the last and one seeded block of every other
+    head.
+For the long-clip layer the mask is given as input (the oracle's per-head
+top-k plus the next 5% as marginal), and the GPU classifier is checked
+against it as well.  Each workload runs as several test items (masks first,
+then groups of heads), so that progress is reported while the oracle works.
 """
 
-import math
 import time
 
 import numpy as np
@@ -17,14 +20,23 @@ import pytest
 import torch
 
 import block_sparse_attention_meanpool_amd as sla
-from gpu_util import REL_L2, check_close, check_lse, counts, f64, rne_bf16_bits, say, to_dev
+from gpu_util import check_close, check_lse, counts, rne_bf16_bits, say, to_dev
 from oracle import sla as osla
 from synth import CONFIGS, generate
 
 pytestmark = pytest.mark.gpu
 
-FULL_OUTPUTS = ("tiny", "short_video")
-SAMPLES_PER_HEAD = {"wan1p3b": 4, "wan14b": 2, "long_clip_95": 1, "long_clip_90": 1}
+FULL_HEADS_LONG = (0, 23)
+# (workload, part): part "masks" runs the path and checks masks and lists;
+# a tuple of heads checks every query block of those heads; "sample" checks
+# three query blocks of each of the other heads
+PARTS = ([("tiny", "masks"), ("tiny", (0, 1)),
+          ("short_video", "masks"), ("short_video", tuple(range(12))),
+          ("wan1p3b", "masks"), ("wan1p3b", tuple(range(12))),
+          ("wan14b", "masks")]
+         + [("wan14b", tuple(range(h, h + 8))) for h in range(0, 40, 8)]
+         + [(n, p) for n in ("long_clip_95", "long_clip_90")
+            for p in ("masks", (FULL_HEADS_LONG[0],), (FULL_HEADS_LONG[1],), "sample")])
 
 
 def _oracle_masks(spec, data):
@@ -43,38 +55,20 @@ def _oracle_masks(spec, data):
     return np.stack(parts).reshape(spec.B, spec.H, spec.nb, spec.nb)
 
 
-def _sample_rows(spec, n_per_head):
-    g = np.random.default_rng(1000 + spec.cfg_id)
-    rows = []
-    for b in range(spec.B):
-        for h in range(spec.H):
-            pick = {0, spec.nb - 1}
-            while len(pick) < min(spec.nb, 2 + n_per_head):
-                pick.add(int(g.integers(0, spec.nb)))
-            rows += [(b, h, i) for i in sorted(pick)]
-    return rows
+_state = {}
 
 
-_cache = {}
-
-
-def _data(spec):
-    if spec.cfg_id not in _cache:
-        _cache.clear()
-        t0 = time.time()
-        _cache[spec.cfg_id] = generate(spec)
-        say(f"  generated cfg {spec.cfg_id} in {time.time() - t0:.1f} s")
-    return _cache[spec.cfg_id]
-
-
-@pytest.mark.timeout(900)
-@pytest.mark.parametrize("name", ["tiny", "short_video", "wan1p3b", "wan14b", "long_clip_95",
-                                  "long_clip_90"])
-def test_workload_parity(name):
+def _run(name):
+    """Inputs, oracle masks and the GPU outputs of one workload, computed once
+    and kept (GPU tensors) for the test items of that workload."""
+    if _state.get("name") == name:
+        return _state
+    _state.clear()
+    torch.cuda.empty_cache()
     spec = CONFIGS[name]
-    say(f"[workload parity] {name}: B={spec.B} H={spec.H} N={spec.N} d={spec.d} b={spec.block} "
-        f"mode={spec.mode}")
-    data = _data(spec)
+    t0 = time.time()
+    data = generate(spec)
+    say(f"  generated {name} in {time.time() - t0:.1f} s")
     t0 = time.time()
     cls_ref = _oracle_masks(spec, data)
     say(f"  oracle masks in {time.time() - t0:.1f} s")
@@ -84,8 +78,7 @@ def test_workload_parity(name):
     b = spec.block
     cls = sla.sla_pool_classify(q, k, b, sel, kc, km, spec.thr or 0.0)
     torch.cuda.synchronize()
-    np.testing.assert_array_equal(cls.cpu().numpy(), cls_ref)
-    say("  class map bit-exact")
+    cls_gpu = cls.cpu().numpy()
     if spec.mode == "maskin":
         cls = torch.from_numpy(cls_ref).cuda()   # the mask is an input here
     kc_max = spec.nb if sel == "cdf" else kc
@@ -100,49 +93,104 @@ def test_workload_parity(name):
         fused, _ = sla.sla_sparse_linear_attn_fwd(q, k, v, b, ci, cc, lin_ws, o_fp32=True)
         del lin_ws
     torch.cuda.synchronize()
-    assert flag.item() == 0
-    idx_ref, cnt_ref = osla.index_lists(cls_ref, osla.CRITICAL, kc_max)
+    del q, k, v
+    _state.update(name=name, spec=spec, data=data, cls_ref=cls_ref, cls_gpu=cls_gpu, kc=kc,
+                  kc_max=kc_max, km=km, flag=int(flag.item()), lists=(ci, cc, mi, mc),
+                  out=(o_s, lse, o_lin, o, fused))
+    return _state
+
+
+def _check_masks(st):
+    spec, cls_ref = st["spec"], st["cls_ref"]
+    np.testing.assert_array_equal(st["cls_gpu"], cls_ref)
+    say("  class map bit-exact")
+    assert st["flag"] == 0
+    ci, cc, mi, mc = st["lists"]
+    idx_ref, cnt_ref = osla.index_lists(cls_ref, osla.CRITICAL, st["kc_max"])
     np.testing.assert_array_equal(ci.cpu().numpy(), idx_ref)
     np.testing.assert_array_equal(cc.cpu().numpy(), cnt_ref)
-    if km:
-        idx_ref, cnt_ref = osla.index_lists(cls_ref, osla.MARGINAL, km)
+    if st["km"]:
+        idx_ref, cnt_ref = osla.index_lists(cls_ref, osla.MARGINAL, st["km"])
         np.testing.assert_array_equal(mi.cpu().numpy(), idx_ref)
         np.testing.assert_array_equal(mc.cpu().numpy(), cnt_ref)
-    say("  lists bit-exact; kept fraction "
-        f"{cc.double().mean().item() / spec.nb:.4f}")
+    say(f"  lists bit-exact; kept fraction {cc.double().mean().item() / spec.nb:.4f}")
 
-    if name in FULL_OUTPUTS:
-        rows = [(bb, h, i) for bb in range(spec.B) for h in range(spec.H) for i in range(spec.nb)]
-    else:
-        rows = _sample_rows(spec, SAMPLES_PER_HEAD[name])
+
+def _rows(st, part):
+    spec = st["spec"]
+    if part == "sample":
+        g = np.random.default_rng(1000 + spec.cfg_id)
+        rows = []
+        for bb in range(spec.B):
+            for h in range(spec.H):
+                if h in FULL_HEADS_LONG:
+                    continue
+                pick = {0, spec.nb - 1, int(g.integers(0, spec.nb))}
+                rows += [(bb, h, i) for i in sorted(pick)]
+        return rows
+    return [(bb, h, i) for bb in range(spec.B) for h in part for i in range(spec.nb)]
+
+
+def _check_outputs(st, part):
+    spec, data, cls_ref, km = st["spec"], st["data"], st["cls_ref"], st["km"]
+    o_s, lse, o_lin, o, fused = st["out"]
+    b = spec.block
+    rows = _rows(st, part)
     t0 = time.time()
-    got_s, got_lse, got_lin, got_o, want_s, want_lse, want_lin, want_o = ([] for _ in range(8))
-    got_f = []
-    heads = {}
+    got = {k: [] for k in ("s", "lse", "lin", "o", "f")}
+    want = {k: [] for k in ("s", "lse", "lin", "o")}
+    head = None
     for (bb, h, i) in rows:
-        if (bb, h) not in heads:
-            heads.clear()
-            heads[(bb, h)] = tuple(osla.bf16_to_f64(data[t][bb, h])[None, None] for t in "qkv")
-        q64, k64, v64 = heads[(bb, h)]
-        res = osla.forward_rows(q64, k64, v64, cls_ref[bb, h][None, None], b, [(0, 0, i)])
-        r_s, r_lse, r_lin, r_o = res[(0, 0, i)]
+        if head != (bb, h):
+            head = (bb, h)
+            q64, k64, v64 = (osla.bf16_to_f64(data[t][bb, h])[None, None] for t in "qkv")
+            g_s, g_lse = o_s[bb, h].cpu().numpy(), lse[bb, h].cpu().numpy()
+            g_lin = None if o_lin is None else o_lin[bb, h].cpu().numpy()
+            g_o = o[bb, h].cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+            g_f = None if fused is None else fused[bb, h].cpu().numpy()
+        r_s, r_lse, r_lin, r_o = osla.forward_rows(q64, k64, v64, cls_ref[bb, h][None, None], b,
+                                                   [(0, 0, i)])[(0, 0, i)]
         lo, hi = osla.block_bounds(spec.N, b, i)
-        want_s.append(r_s); want_lse.append(r_lse); want_lin.append(r_lin); want_o.append(r_o)
-        got_s.append(o_s[bb, h, lo:hi].cpu().numpy())
-        got_lse.append(lse[bb, h, lo:hi].cpu().numpy())
-        got_lin.append(np.zeros_like(r_lin) if o_lin is None else o_lin[bb, h, lo:hi].cpu().numpy())
-        got_o.append(o[bb, h, lo:hi].cpu().contiguous().view(torch.int16).numpy().view(np.uint16))
-        if fused is not None:
-            got_f.append(fused[bb, h, lo:hi].cpu().numpy())
-    say(f"  oracle outputs for {len(rows)} query blocks in {time.time() - t0:.1f} s")
+        for key, val in (("s", r_s), ("lse", r_lse), ("lin", r_lin), ("o", r_o)):
+            want[key].append(val)
+        got["s"].append(g_s[lo:hi])
+        got["lse"].append(g_lse[lo:hi])
+        got["lin"].append(np.zeros_like(r_lin) if g_lin is None else g_lin[lo:hi])
+        got["o"].append(g_o[lo:hi])
+        if g_f is not None:
+            got["f"].append(g_f[lo:hi])
+    heads = sorted({h for (_, h, _) in rows})
+    say(f"  oracle outputs for {len(rows)} query blocks of heads {heads[0]}..{heads[-1]} "
+        f"({len(heads)} heads) in {time.time() - t0:.1f} s")
     cat = np.concatenate
-    check_close(cat(got_s), cat(want_s), "O_s")
-    check_lse(cat(got_lse), cat(want_lse))
+    check_close(cat(got["s"]), cat(want["s"]), "O_s")
+    check_lse(cat(got["lse"]), cat(want["lse"]))
     if km:
-        check_close(cat(got_lin), cat(want_lin), "O_lin")
-    pre = (cat(got_s) + cat(got_lin)).astype(np.float32)
-    check_close(pre, cat(want_o), "O (fp32, pre-rounding)")
-    np.testing.assert_array_equal(cat(got_o), rne_bf16_bits(pre))
-    check_close(osla.bf16_to_f64(cat(got_o)), cat(want_o), "O (bf16)", max_abs=4e-2, rel_l2=8e-3)
-    if fused is not None:
-        check_close(cat(got_f), cat(want_o), "O fused (fp32)")
+        check_close(cat(got["lin"]), cat(want["lin"]), "O_lin")
+    pre = (cat(got["s"]) + cat(got["lin"])).astype(np.float32)
+    check_close(pre, cat(want["o"]), "O (fp32, pre-rounding)")
+    np.testing.assert_array_equal(cat(got["o"]), rne_bf16_bits(pre))
+    check_close(osla.bf16_to_f64(cat(got["o"])), cat(want["o"]), "O (bf16)", max_abs=4e-2,
+                rel_l2=8e-3)
+    if got["f"]:
+        check_close(cat(got["f"]), cat(want["o"]), "O fused (fp32)")
+
+
+def _id(p):
+    name, part = p
+    if isinstance(part, tuple):
+        part = f"heads{part[0]}-{part[-1]}" if len(part) > 1 else f"head{part[0]}"
+    return f"{name}-{part}"
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,part", PARTS, ids=[_id(p) for p in PARTS])
+def test_workload_parity(name, part):
+    spec = CONFIGS[name]
+    say(f"[workload parity] {name} ({part}): B={spec.B} H={spec.H} N={spec.N} d={spec.d} "
+        f"b={spec.block} mode={spec.mode}")
+    st = _run(name)
+    if part == "masks":
+        _check_masks(st)
+    else:
+        _check_outputs(st, part)
