@@ -25,6 +25,11 @@ Printed JSON line:
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--config wan14b]
                 [--no-cpu-baseline] [--no-dense] [--profile] [--unfused]
+                [--keep F]
+
+--keep F replaces a top-k workload's kept fraction (the sparsity sweep that
+checks the kernel's time and MFMA work scale with the kept tiles); the line
+then describes that workload, not the headline one.
 """
 
 import argparse
@@ -76,7 +81,7 @@ def pipe_mfma_flop(crit_idx, crit_cnt, N):
 
 # Sources of the sparse-attention kernel; a counter summary applies only to the
 # build whose sources hash to the value recorded in it.
-KERNEL_SOURCES = ["sparse_attn.hip", "common.h", "linear_apply.h"]
+KERNEL_SOURCES = ["sparse_attn.hip", "common.h", "linear_apply.h", "lists.h"]
 
 
 def kernel_source_hash():
@@ -240,6 +245,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip the backward timing")
     ap.add_argument("--unfused", action="store_true",
                     help="with a linear branch: separate sparse, linear and combine calls")
+    ap.add_argument("--keep", default=None,
+                    help="kept fraction for a top-k workload, e.g. 1/10 (sparsity sweep)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the path shards by "
@@ -256,6 +263,13 @@ def main():
     from synth import CONFIGS, generate
 
     spec = CONFIGS[args.config]
+    if args.keep is not None:
+        import dataclasses
+        from fractions import Fraction
+        if spec.mode != "topk":
+            log("[bench] --keep applies to top-k workloads only")
+            sys.exit(2)
+        spec = dataclasses.replace(spec, keep=Fraction(args.keep))
     B, H, N, d, b, nb = spec.B, spec.H, spec.N, spec.d, spec.block, spec.nb
     sel = "sla3" if spec.mode == "maskin" else spec.mode
     kc, km = sla.counts_for(sel, nb, spec.keep, spec.marg)
