@@ -4,8 +4,8 @@ Workload: the Wan-14B-like layer (B=1, H=40, N=75600 = 21 x 45 x 80 tokens,
 d=128, 128-token blocks), top-k key tiles at 95% sparsity, bf16 inputs from
 the seeded generator (already resident in HBM when timing starts).
 
-A step is one pass of the whole path: pool + classify, list compaction,
-sparse attention (bf16 output written directly: this workload has no
+A step is one pass of the whole path: pool + classify, list compaction (and
+the query-block run order, sla_row_order, timed with it), sparse attention (bf16 output written directly: this workload has no
 marginal tiles, so the linear branch and the sum are empty).  Workloads
 with marginal tiles (--config wan1p3b, long_clip_95, long_clip_90) run the
 linear branch's preparation and then the fused sparse + linear kernel that
@@ -116,7 +116,7 @@ def measured_traffic(config_name):
 
 
 def backward_timing(sla, torch, q, k, v, b, crit_idx, crit_cnt, marg_idx, marg_cnt, km, flop,
-                    steps, stream):
+                    steps, stream, order=None):
     """Gradients of the whole layer (mask held fixed) for a seeded dO: the
     softmax branch's backward and, with marginal tiles, the linear branch's,
     each timed with HIP events on the launch stream.  The forward's O_s and
@@ -124,7 +124,7 @@ def backward_timing(sla, torch, q, k, v, b, crit_idx, crit_cnt, marg_idx, marg_c
     g = torch.Generator(device=q.device).manual_seed(7)
     d_o = torch.randn(q.shape, generator=g, device=q.device, dtype=torch.float32).to(torch.bfloat16)
     o_s, lse = sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt, o_fp32=False,
-                                       want_lse=True)
+                                       want_lse=True, row_order=order)
     dq, dk, dv = (torch.empty(q.shape, dtype=torch.float32, device=q.device) for _ in range(3))
     B, H, N, d = q.shape
     ws = torch.empty(sla.lib().sla_sparse_attn_bwd_ws_bytes(B, H, N, d, b), dtype=torch.uint8,
@@ -139,7 +139,7 @@ def backward_timing(sla, torch, q, k, v, b, crit_idx, crit_cnt, marg_idx, marg_c
         if marks:
             marks[0].record(stream)
         sla.sla_sparse_attn_bwd(q, k, v, b, crit_idx, crit_cnt, o_s, lse, d_o, dq=dq, dk=dk, dv=dv,
-                                ws=ws)
+                                ws=ws, row_order=order)
         if marks:
             marks[1].record(stream)
         if km:
@@ -298,6 +298,7 @@ def main():
         lin_ws = torch.empty(sla.lib().sla_linear_branch_ws_bytes(B, H, N, d, b), dtype=torch.uint8,
                              device=dev)
     o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+    order = torch.empty((B, H, nb), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     fused = bool(km) and not args.unfused
@@ -315,17 +316,19 @@ def main():
         if record:
             marks[1].record(stream)
         sla.sla_block_mask(cls, kc_max, km, crit_idx, crit_cnt, marg_idx, marg_cnt)
+        sla.sla_row_order(crit_idx, crit_cnt, order)
         if record:
             marks[2].record(stream)
         if fused:
             sla.sla_linear_branch_prepare(k, v, b, marg_idx, marg_cnt, ws=lin_ws)
             if record:
                 marks[3].record(stream)
-            sla.sla_sparse_linear_attn_fwd(q, k, v, b, crit_idx, crit_cnt, lin_ws, o=o)
+            sla.sla_sparse_linear_attn_fwd(q, k, v, b, crit_idx, crit_cnt, lin_ws, o=o,
+                                           row_order=order)
             if record:
                 marks[4].record(stream)
         elif km:
-            sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt, o_s=o_s)
+            sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt, o_s=o_s, row_order=order)
             if record:
                 marks[3].record(stream)
             sla.sla_linear_branch_fwd(q, k, v, b, marg_idx, marg_cnt, o_lin=o_lin, ws=lin_ws)
@@ -335,7 +338,7 @@ def main():
             if record:
                 marks[5].record(stream)
         else:
-            sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt, o_s=o)
+            sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt, o_s=o, row_order=order)
             if record:
                 marks[3].record(stream)
         if record:
@@ -425,7 +428,7 @@ def main():
 
     if not args.no_backward:
         extra["backward"] = backward_timing(sla, torch, q, k, v, b, crit_idx, crit_cnt, marg_idx,
-                                            marg_cnt, km, flop, args.steps, stream)
+                                            marg_cnt, km, flop, args.steps, stream, order)
         log(f"[bench] backward: {extra['backward']}")
 
     if not args.no_dense:

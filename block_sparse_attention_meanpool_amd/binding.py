@@ -41,18 +41,18 @@ _SIGS = {
                                          _F, _F, _P, _P, _P, _P]),
     "sla_pool_classify_noalloc_scratch_bytes": (_SZ, []),
     "sla_block_mask": (_I32, [_P, _I64, _I64, _I64, _I64, _P, _P, _I32, _P, _P, _I32, _P, _P]),
-    "sla_sparse_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _F,
-                                   _P, _I32, _P, _P]),
+    "sla_sparse_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _P,
+                                   _F, _P, _I32, _P, _P]),
     "sla_linear_branch_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _P,
                                      _P, _SZ, _P]),
     "sla_linear_branch_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32]),
     "sla_linear_branch_prepare": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _P,
                                          _SZ, _P]),
     "sla_sparse_linear_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32,
-                                          _F, _P, _SZ, _P, _I32, _P, _P]),
+                                          _P, _F, _P, _SZ, _P, _I32, _P, _P]),
     "sla_combine": (_I32, [_P, _I32, _P, _P, _I64, _P]),
-    "sla_sparse_attn_bwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _F, _P,
-                                   _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "sla_sparse_attn_bwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _P, _F,
+                                   _P, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "sla_sparse_attn_bwd_ws_bytes": (_SZ, [_I64, _I64, _I64, _I64, _I32]),
     "sla_linear_branch_bwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _P, _P, _I32, _P, _P,
                                      _SZ, _P, _P, _P, _P, _SZ, _P]),
@@ -63,6 +63,7 @@ _SIGS = {
     "sla_tile_permute": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I32, _P]),
     "sla_dense_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _F, _P, _I32, _P, _P]),
     "sla_check_lists": (_I32, [_P, _P, _I64, _I32, _I64, _P, _P]),
+    "sla_row_order": (_I32, [_P, _P, _I64, _I64, _I64, _I32, _P, _P]),
     "sla_debug_flag": (_P, []),
     "sla_status_string": (ctypes.c_char_p, [_I32]),
     "sla_version": (_I32, []),
@@ -257,12 +258,14 @@ def sla_block_mask(cls, kc_max, km_max=0, crit_idx=None, crit_cnt=None, marg_idx
     return crit_idx, crit_cnt, marg_idx, marg_cnt
 
 
-def _attn_args(q, k, v, block, lists=(), outs=(), lse=None):
+def _attn_args(q, k, v, block, lists=(), outs=(), lse=None, row_order=None):
     """Shape and device checks shared by the attention wrappers: k and v (and
     any extra [B, H, N, d] buffers in outs, given as (tensor, name, dtypes))
-    like q; each (idx, cnt, name) list of lists; lse [B, H, N]."""
+    like q; each (idx, cnt, name) list of lists; lse [B, H, N]; a row order
+    [B, H, nb]."""
     B, H, N, d = _qshape(q)
     nb = num_blocks(N, block)
+    _shape(row_order, (B, H, nb), "row_order")
     for t, n in ((k, "k"), (v, "v")):
         if t is not None:
             _shape(t, q.shape, n)
@@ -283,6 +286,8 @@ def _attn_args(q, k, v, block, lists=(), outs=(), lse=None):
             _dev(t, dt, n, q.device)
     if lse is not None:
         _dev(lse, torch.float32, "lse", q.device)
+    if row_order is not None:
+        _dev(row_order, torch.int32, "row_order", q.device)
     return B, H, N, d, nb
 
 
@@ -290,9 +295,9 @@ _O_TYPES = (torch.float32, torch.bfloat16)
 
 
 def sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, scale=None, o_s=None, o_fp32=True,
-                        lse=None, want_lse=False, stream=None):
+                        lse=None, want_lse=False, row_order=None, stream=None):
     B, H, N, d, _ = _attn_args(q, k, v, block, [(crit_idx, crit_cnt, "crit")],
-                               [(o_s, "o_s", _O_TYPES)], lse)
+                               [(o_s, "o_s", _O_TYPES)], lse, row_order)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     if o_s is None:
@@ -300,7 +305,7 @@ def sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, scale=None, o_s=None
     if want_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _call("sla_sparse_attn_fwd", _ptr(q), _ptr(k), _ptr(v), B, H, N, d, block, _ptr(crit_idx),
-          _ptr(crit_cnt), crit_idx.shape[-1], float(scale), _ptr(o_s),
+          _ptr(crit_cnt), crit_idx.shape[-1], _ptr(row_order), float(scale), _ptr(o_s),
           int(o_s.dtype == torch.float32), _ptr(lse), _stream(stream))
     return o_s, lse
 
@@ -349,9 +354,9 @@ def sla_linear_branch_prepare(k, v, block, marg_idx, marg_cnt, ws=None, stream=N
 
 
 def sla_sparse_linear_attn_fwd(q, k, v, block, crit_idx, crit_cnt, lin_ws, scale=None, o=None,
-                               o_fp32=False, lse=None, want_lse=False, stream=None):
+                               o_fp32=False, lse=None, want_lse=False, row_order=None, stream=None):
     B, H, N, d, _ = _attn_args(q, k, v, block, [(crit_idx, crit_cnt, "crit")],
-                               [(o, "o", _O_TYPES)], lse)
+                               [(o, "o", _O_TYPES)], lse, row_order)
     _dev(lin_ws, torch.uint8, "lin_ws", q.device)
     if scale is None:
         scale = 1.0 / math.sqrt(d)
@@ -360,19 +365,20 @@ def sla_sparse_linear_attn_fwd(q, k, v, block, crit_idx, crit_cnt, lin_ws, scale
     if want_lse and lse is None:
         lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
     _call("sla_sparse_linear_attn_fwd", _ptr(q), _ptr(k), _ptr(v), B, H, N, d, block,
-          _ptr(crit_idx), _ptr(crit_cnt), crit_idx.shape[-1], float(scale), _ptr(lin_ws),
+          _ptr(crit_idx), _ptr(crit_cnt), crit_idx.shape[-1], _ptr(row_order), float(scale),
+          _ptr(lin_ws),
           lin_ws.numel(), _ptr(o), int(o.dtype == torch.float32), _ptr(lse), _stream(stream))
     return o, lse
 
 
 def sla_sparse_attn_bwd(q, k, v, block, crit_idx, crit_cnt, o_s, lse, d_o, scale=None, dq=None,
-                        dk=None, dv=None, ws=None, stream=None):
+                        dk=None, dv=None, ws=None, row_order=None, stream=None):
     if o_s is None or lse is None or d_o is None:
         raise ValueError("o_s, lse and d_o are required")
     B, H, N, d, _ = _attn_args(q, k, v, block, [(crit_idx, crit_cnt, "crit")],
                                [(o_s, "o_s", _O_TYPES), (d_o, "d_o", torch.bfloat16),
                                 (dq, "dq", torch.float32), (dk, "dk", torch.float32),
-                                (dv, "dv", torch.float32)], lse)
+                                (dv, "dv", torch.float32)], lse, row_order)
     if ws is not None:
         _dev(ws, torch.uint8, "ws", q.device)
     if scale is None:
@@ -383,7 +389,7 @@ def sla_sparse_attn_bwd(q, k, v, block, crit_idx, crit_cnt, o_s, lse, d_o, scale
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _call("sla_sparse_attn_bwd", _ptr(q), _ptr(k), _ptr(v), B, H, N, d, block, _ptr(crit_idx),
-          _ptr(crit_cnt), crit_idx.shape[-1], float(scale), _ptr(o_s),
+          _ptr(crit_cnt), crit_idx.shape[-1], _ptr(row_order), float(scale), _ptr(o_s),
           int(o_s.dtype == torch.float32), _ptr(lse), _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv),
           _ptr(ws), ws.numel() * ws.element_size(), _stream(stream))
     return dq, dk, dv
@@ -483,6 +489,22 @@ def sla_check_lists(idx, cnt, nkb, err_flag=None, stream=None):
     return err_flag
 
 
+def sla_row_order(idx, cnt, order=None, stream=None):
+    """Per head, the query blocks sorted by the median tile of their lists
+    (int32 [B, H, nqb], a permutation per head): the run order to pass as
+    row_order.  Scheduling only; results do not depend on it."""
+    B, H, nqb, width = _qshape(idx, "idx")
+    _shape(cnt, (B, H, nqb), "cnt")
+    _shape(order, (B, H, nqb), "order")
+    _dev(idx, torch.int32, "idx")
+    _dev(cnt, torch.int32, "cnt", idx.device)
+    if order is None:
+        order = torch.empty((B, H, nqb), dtype=torch.int32, device=idx.device)
+    _dev(order, torch.int32, "order", idx.device)
+    _call("sla_row_order", _ptr(idx), _ptr(cnt), B, H, nqb, width, _ptr(order), _stream(stream))
+    return order
+
+
 def debug_flag_address():
     """Device address of the debug flag word (library built with
     SLA_DEBUG_CHECKS), or None for the release build."""
@@ -525,9 +547,10 @@ def _select(q, k, block, mode, keep, marg, thr, cls, stream):
 def forward(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=None, o_fp32=False,
             fused=False, stream=None):
     """Pool and classify (unless `cls` is given: mask-in), compact the lists,
-    run the sparse and linear branches and combine.  With fused=True and a
-    linear branch, the two branches run as sla_linear_branch_prepare plus
-    sla_sparse_linear_attn_fwd (no O_s / O_lin intermediates).
+    order the query blocks for L2 locality (sla_row_order), run the sparse and
+    linear branches and combine.  With fused=True and a linear branch, the two
+    branches run as sla_linear_branch_prepare plus sla_sparse_linear_attn_fwd
+    (no O_s / O_lin intermediates).
 
     mode "topk" (keep), "cdf" (thr), "sla3" (keep, marg).  With a given cls,
     `keep`/`marg` only size the lists (default: the whole row).
@@ -535,23 +558,25 @@ def forward(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=Non
     """
     cls, crit_idx, crit_cnt, marg_idx, marg_cnt = _select(q, k, block, mode, keep, marg, thr, cls,
                                                           stream)
+    order = sla_row_order(crit_idx, crit_cnt, stream=stream)
     km_max = 0 if marg_idx is None else marg_idx.shape[-1]
     out = {"cls": cls, "crit_idx": crit_idx, "crit_cnt": crit_cnt, "marg_idx": marg_idx,
-           "marg_cnt": marg_cnt}
+           "marg_cnt": marg_cnt, "row_order": order}
+    attn = dict(row_order=order, stream=stream)
     if km_max and fused:
         lin_ws = sla_linear_branch_prepare(k, v, block, marg_idx, marg_cnt, stream=stream)
-        o, _ = sla_sparse_linear_attn_fwd(q, k, v, block, crit_idx, crit_cnt, lin_ws, stream=stream)
+        o, _ = sla_sparse_linear_attn_fwd(q, k, v, block, crit_idx, crit_cnt, lin_ws, **attn)
         out.update(o=o)
     elif km_max:
-        o_s, _ = sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, o_fp32=True, stream=stream)
+        o_s, _ = sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, o_fp32=True, **attn)
         o_lin = sla_linear_branch_fwd(q, k, v, block, marg_idx, marg_cnt, stream=stream)
         o = sla_combine(o_s, o_lin, stream=stream)
         out.update(o_s=o_s, o_lin=o_lin, o=o)
     elif o_fp32:
-        o_s, _ = sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, o_fp32=True, stream=stream)
+        o_s, _ = sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, o_fp32=True, **attn)
         out.update(o_s=o_s, o=sla_combine(o_s, None, stream=stream))
     else:
-        o, _ = sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, o_fp32=False, stream=stream)
+        o, _ = sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, o_fp32=False, **attn)
         out.update(o=o)
     return out
 
@@ -567,12 +592,14 @@ class SlaAttention(torch.autograd.Function):
     LSE kept for the backward), sla_linear_branch_fwd, sla_combine.  Backward:
     sla_sparse_attn_bwd, then sla_linear_branch_bwd adds the linear branch's
     gradients; they are fp32, and autograd rounds them to the inputs' bf16.
-    marg_idx / marg_cnt may be None (no linear branch)."""
+    marg_idx / marg_cnt may be None (no linear branch); row_order (from
+    sla_row_order) may be None and only sets the kernels' schedule."""
 
     @staticmethod
-    def forward(ctx, q, k, v, block, crit_idx, crit_cnt, marg_idx=None, marg_cnt=None):
+    def forward(ctx, q, k, v, block, crit_idx, crit_cnt, marg_idx=None, marg_cnt=None,
+                row_order=None):
         o_s, lse = sla_sparse_attn_fwd(q, k, v, block, crit_idx, crit_cnt, o_fp32=True,
-                                       want_lse=True)
+                                       want_lse=True, row_order=row_order)
         lin_ws = None
         o_lin = None
         if marg_idx is not None:
@@ -582,19 +609,21 @@ class SlaAttention(torch.autograd.Function):
             o_lin = sla_linear_branch_fwd(q, k, v, block, marg_idx, marg_cnt, ws=lin_ws)
         o = sla_combine(o_s, o_lin)
         ctx.block = block
-        ctx.save_for_backward(q, k, v, crit_idx, crit_cnt, marg_idx, marg_cnt, o_s, lse, lin_ws)
+        ctx.save_for_backward(q, k, v, crit_idx, crit_cnt, marg_idx, marg_cnt, o_s, lse, lin_ws,
+                              row_order)
         return o
 
     @staticmethod
     def backward(ctx, d_o):
-        q, k, v, crit_idx, crit_cnt, marg_idx, marg_cnt, o_s, lse, lin_ws = ctx.saved_tensors
+        q, k, v, crit_idx, crit_cnt, marg_idx, marg_cnt, o_s, lse, lin_ws, order = ctx.saved_tensors
         if d_o.dtype != torch.bfloat16:
             raise ValueError(f"the output gradient must be bf16, got {d_o.dtype}")
         d_o = d_o.contiguous()
-        dq, dk, dv = sla_sparse_attn_bwd(q, k, v, ctx.block, crit_idx, crit_cnt, o_s, lse, d_o)
+        dq, dk, dv = sla_sparse_attn_bwd(q, k, v, ctx.block, crit_idx, crit_cnt, o_s, lse, d_o,
+                                         row_order=order)
         if marg_idx is not None:
             sla_linear_branch_bwd(q, k, v, ctx.block, marg_idx, marg_cnt, d_o, lin_ws, dq, dk, dv)
-        return dq, dk, dv, None, None, None, None, None
+        return dq, dk, dv, None, None, None, None, None, None
 
 
 def sla_attention(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, cls=None):
@@ -604,5 +633,6 @@ def sla_attention(q, k, v, block, mode="topk", keep=None, marg=None, thr=None, c
     crit_cnt, marg_idx, marg_cnt)."""
     with torch.no_grad():
         lists = _select(q.detach(), k.detach(), block, mode, keep, marg, thr, cls, None)
-    _, crit_idx, crit_cnt, marg_idx, marg_cnt = lists
-    return SlaAttention.apply(q, k, v, block, crit_idx, crit_cnt, marg_idx, marg_cnt), lists
+        _, crit_idx, crit_cnt, marg_idx, marg_cnt = lists
+        order = sla_row_order(crit_idx, crit_cnt)
+    return SlaAttention.apply(q, k, v, block, crit_idx, crit_cnt, marg_idx, marg_cnt, order), lists

@@ -12,6 +12,7 @@ constexpr int64_t kMaxBlocks = 4096;
 constexpr int64_t kMaxHeads = 65535;  // B*H: grid y/z extent of the pooling and score launches
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -108,6 +109,15 @@ sla_status debug_check_lists(const int32_t* idx, const int32_t* cnt, int64_t row
 }  // namespace
 
 extern "C" {
+
+sla_status sla_row_order(const int32_t* idx, const int32_t* cnt, int64_t B, int64_t H,
+                         int64_t nqb, int32_t width, int32_t* order, hipStream_t stream) {
+  if (!idx || !cnt || !order) return SLA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || nqb < 1 || nqb > kMaxBlocks || width < 1) return SLA_ERR_INVALID_ARG;
+  if (B * H > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
+  if (!aligned4(idx) || !aligned4(cnt) || !aligned4(order)) return SLA_ERR_ALIGNMENT;
+  return from_hip(sla::launch_row_order(idx, cnt, B * H, (int)nqb, width, order, stream));
+}
 
 sla_status sla_check_lists(const int32_t* idx, const int32_t* cnt, int64_t rows, int32_t width,
                            int64_t nkb, int32_t* err_flag, hipStream_t stream) {
@@ -206,8 +216,8 @@ sla_status sla_block_mask(const uint8_t* cls, int64_t B, int64_t H, int64_t nqb,
 sla_status sla_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                                int64_t H, int64_t N, int64_t d, int32_t block,
                                const int32_t* crit_idx, const int32_t* crit_cnt, int32_t kc_max,
-                               float scale, void* o_s, int32_t o_is_fp32, float* lse,
-                               hipStream_t stream) {
+                               const int32_t* row_order, float scale, void* o_s, int32_t o_is_fp32,
+                               float* lse, hipStream_t stream) {
   int64_t nb = 0;
   sla_status st = check_shape(B, H, N, d, block, &nb);
   if (st != SLA_OK) return st;
@@ -215,10 +225,11 @@ sla_status sla_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
   if (kc_max < 1 || kc_max > nb) return SLA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_s)) return SLA_ERR_ALIGNMENT;
+  if (!aligned4(row_order)) return SLA_ERR_ALIGNMENT;
   SLA_DEBUG_LISTS(crit_idx, crit_cnt, B * H * nb, kc_max, nb, stream);
   return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
                                    crit_cnt, kc_max, scale, o_s, o_is_fp32 != 0, lse, nullptr,
-                                   stream));
+                                   row_order, stream));
 }
 
 sla_status sla_dense_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
@@ -231,7 +242,8 @@ sla_status sla_dense_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16
   if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SLA_ERR_ALIGNMENT;
   return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, nullptr, nullptr,
-                                   (int)nb, scale, o, o_is_fp32 != 0, lse, nullptr, stream));
+                                   (int)nb, scale, o, o_is_fp32 != 0, lse, nullptr, nullptr,
+                                   stream));
 }
 
 size_t sla_linear_branch_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {
@@ -280,7 +292,8 @@ sla_status sla_linear_branch_fwd(const uint16_t* q, const uint16_t* k, const uin
 sla_status sla_sparse_linear_attn_fwd(const uint16_t* q, const uint16_t* k, const uint16_t* v,
                                       int64_t B, int64_t H, int64_t N, int64_t d, int32_t block,
                                       const int32_t* crit_idx, const int32_t* crit_cnt,
-                                      int32_t kc_max, float scale, const void* lin_ws,
+                                      int32_t kc_max, const int32_t* row_order, float scale,
+                                      const void* lin_ws,
                                       size_t lin_ws_bytes, void* o, int32_t o_is_fp32, float* lse,
                                       hipStream_t stream) {
   int64_t nb = 0;
@@ -292,10 +305,11 @@ sla_status sla_sparse_linear_attn_fwd(const uint16_t* q, const uint16_t* k, cons
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SLA_ERR_ALIGNMENT;
   const size_t need = sla_linear_branch_ws_bytes(B, H, N, d, block);
   if (!lin_ws || lin_ws_bytes < need || !aligned16(lin_ws)) return SLA_ERR_WORKSPACE;
+  if (!aligned4(row_order)) return SLA_ERR_ALIGNMENT;
   SLA_DEBUG_LISTS(crit_idx, crit_cnt, B * H * nb, kc_max, nb, stream);
   return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
                                    crit_cnt, kc_max, scale, o, o_is_fp32 != 0, lse, lin_ws,
-                                   stream));
+                                   row_order, stream));
 }
 
 size_t sla_sparse_attn_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {
@@ -307,7 +321,8 @@ size_t sla_sparse_attn_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, 
 sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t B,
                                int64_t H, int64_t N, int64_t d, int32_t block,
                                const int32_t* crit_idx, const int32_t* crit_cnt, int32_t kc_max,
-                               float scale, const void* o_s, int32_t o_s_is_fp32, const float* lse,
+                               const int32_t* row_order, float scale, const void* o_s,
+                               int32_t o_s_is_fp32, const float* lse,
                                const uint16_t* d_o, float* dq, float* dk, float* dv, void* ws,
                                size_t ws_bytes, hipStream_t stream) {
   int64_t nb = 0;
@@ -318,7 +333,7 @@ sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
   if (kc_max < 1 || kc_max > nb) return SLA_ERR_INVALID_ARG;
   if (!(scale > 0.f) || scale == INFINITY) return SLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_s) || !aligned16(d_o) ||
-      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || (reinterpret_cast<uintptr_t>(lse) & 3u))
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse) || !aligned4(row_order))
     return SLA_ERR_ALIGNMENT;
   const int64_t BH = B * H;
   if ((BH * nb * kc_max + 255) / 256 > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
@@ -327,7 +342,7 @@ sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
   SLA_DEBUG_LISTS(crit_idx, crit_cnt, BH * nb, kc_max, nb, stream);
   return from_hip(sla::launch_attn_bwd(q, k, v, BH, (int)N, (int)d, block, (int)nb, crit_idx,
                                        crit_cnt, kc_max, scale, o_s, o_s_is_fp32 != 0, lse, d_o,
-                                       dq, dk, dv, ws, stream));
+                                       dq, dk, dv, ws, row_order, stream));
 }
 
 size_t sla_linear_branch_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block) {
@@ -438,6 +453,6 @@ const char* sla_status_string(sla_status status) {
   }
 }
 
-int32_t sla_version(void) { return 300; }
+int32_t sla_version(void) { return 400; }
 
 }  // extern "C"

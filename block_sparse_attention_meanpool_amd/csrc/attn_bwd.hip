@@ -166,7 +166,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const void* __restrict__ o_s, int o_fp32, const float* __restrict__ lse,
     const uint16_t* __restrict__ d_o, int N, int nqb, int nkb, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, int kmax, float sl2, float scale, float* __restrict__ dq,
-    float* __restrict__ Dbuf, int seg) {
+    float* __restrict__ Dbuf, int seg, const int32_t* __restrict__ order) {
   __shared__ __attribute__((aligned(1024))) char K0[BUFB];
   __shared__ __attribute__((aligned(1024))) char V0[BUFB];
   __shared__ __attribute__((aligned(1024))) char K1[BUFB];
@@ -175,8 +175,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int64_t bh = slot / seg;
-  const int qb = xcd * seg + slot % seg;
-  if (qb >= nqb) return;
+  const int pos = xcd * seg + slot % seg;
+  if (pos >= nqb) return;
+  const int qb = ordered_block(order, bh, nqb, pos);
+  if (qb < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int64_t head_off = bh * (int64_t)N * D;
@@ -467,7 +469,7 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int kmax,
                            float scale, const void* o_s, int o_fp32, const float* lse,
                            const uint16_t* d_o, float* dq, float* dk, float* dv, void* ws,
-                           hipStream_t s) {
+                           const int32_t* order, hipStream_t s) {
   const AttnBwdWs lw = attn_bwd_ws_layout(BH, N, nb);
   char* p = static_cast<char*>(ws);
   float* Dbuf = reinterpret_cast<float*>(p);
@@ -484,12 +486,12 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   if (e != hipSuccess) return e;
   if (d != bwd::D || block != bwd::BLK)
     return launch_attn_bwd_generic(q, k, v, BH, N, d, block, nb, idx, cnt, kmax, scale, o_s, o_fp32,
-                                   lse, d_o, dq, dk, dv, Dbuf, col_idx, col_cnt, s);
+                                   lse, d_o, dq, dk, dv, Dbuf, col_idx, col_cnt, order, s);
   const int seg = (nb + 7) / 8;
   const dim3 grid((unsigned)(BH * seg * 8));
   const float sl2 = scale * kLog2e;
   bwd::attn_bwd_dq_kernel<<<grid, bwd::NT, 0, s>>>(q, k, v, o_s, o_fp32, lse, d_o, N, nb, nb, idx,
-                                                   cnt, kmax, sl2, scale, dq, Dbuf, seg);
+                                                   cnt, kmax, sl2, scale, dq, Dbuf, seg, order);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   bwd::attn_bwd_dkdv_kernel<<<grid, bwd::NT, 0, s>>>(q, k, v, lse, Dbuf, d_o, N, nb, nb, col_idx,

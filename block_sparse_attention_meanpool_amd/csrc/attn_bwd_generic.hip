@@ -44,7 +44,7 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(
     const void* __restrict__ o_s, int o_fp32, const float* __restrict__ lse,
     const uint16_t* __restrict__ d_o, int N, int nqb, int nkb, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, int kmax, float sl2, float scale, float* __restrict__ dq,
-    float* __restrict__ Dbuf, int seg) {
+    float* __restrict__ Dbuf, int seg, const int32_t* __restrict__ order) {
   constexpr int CH = D / 8, KS = D / 16, KB = BLK / 32;
   __shared__ __attribute__((aligned(16))) char Ks[BLK * D * 2];
   __shared__ __attribute__((aligned(16))) char Kt[D * BLK * 2];
@@ -53,8 +53,10 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int64_t bh = slot / seg;
-  const int qb = xcd * seg + slot % seg;
-  if (qb >= nqb) return;
+  const int pos = xcd * seg + slot % seg;
+  if (pos >= nqb) return;
+  const int qb = ordered_block(order, bh, nqb, pos);
+  if (qb < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int64_t head_off = bh * (int64_t)N * D;
@@ -292,12 +294,13 @@ static hipError_t launch_t(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
                            float scale, const void* o_s, int o_fp32, const float* lse,
                            const uint16_t* d_o, float* dq, float* dk, float* dv, float* Dbuf,
-                           const uint16_t* col_idx, const int32_t* col_cnt, hipStream_t s) {
+                           const uint16_t* col_idx, const int32_t* col_cnt, const int32_t* order,
+                           hipStream_t s) {
   const int seg = (nb + 7) / 8;
   const dim3 grid((unsigned)(BH * seg * 8));
   const float sl2 = scale * kLog2e;
   dq_kernel<D, BLK><<<grid, BLK * 2, 0, s>>>(q, k, v, o_s, o_fp32, lse, d_o, N, nb, nb, idx, cnt,
-                                              kmax, sl2, scale, dq, Dbuf, seg);
+                                              kmax, sl2, scale, dq, Dbuf, seg, order);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dkdv_kernel<D, BLK><<<grid, BLK * 2, 0, s>>>(q, k, v, lse, Dbuf, d_o, N, nb, nb, col_idx, col_cnt,
@@ -313,16 +316,16 @@ hipError_t launch_attn_bwd_generic(const uint16_t* q, const uint16_t* k, const u
                                    const void* o_s, int o_fp32, const float* lse,
                                    const uint16_t* d_o, float* dq, float* dk, float* dv,
                                    float* Dbuf, const uint16_t* col_idx, const int32_t* col_cnt,
-                                   hipStream_t s) {
+                                   const int32_t* order, hipStream_t s) {
   if (d == 64 && block == 64)
     return gbwd::launch_t<64, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o_s, o_fp32, lse, d_o,
-                                  dq, dk, dv, Dbuf, col_idx, col_cnt, s);
+                                  dq, dk, dv, Dbuf, col_idx, col_cnt, order, s);
   if (d == 64 && block == 128)
     return gbwd::launch_t<64, 128>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o_s, o_fp32, lse,
-                                   d_o, dq, dk, dv, Dbuf, col_idx, col_cnt, s);
+                                   d_o, dq, dk, dv, Dbuf, col_idx, col_cnt, order, s);
   if (d == 128 && block == 64)
     return gbwd::launch_t<128, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o_s, o_fp32, lse,
-                                   d_o, dq, dk, dv, Dbuf, col_idx, col_cnt, s);
+                                   d_o, dq, dk, dv, Dbuf, col_idx, col_cnt, order, s);
   return hipErrorInvalidValue;
 }
 

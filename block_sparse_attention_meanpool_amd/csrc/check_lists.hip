@@ -1,8 +1,17 @@
-// Validation of per-query-block tile lists supplied by a caller (the lists
-// the block-mask kernel writes always pass): every entry in [0, nkb), no
-// repeated entry, ascending order, and a count in [0, width].  The kernels
-// that read lists treat a list as a set of tiles whatever it holds; this check
-// tells a caller that its lists were not in the documented form.
+// Per-query-block tile lists (the Veda article's per-query sets of key
+// tiles): validation of lists supplied by a caller, and a locality-aware order
+// in which to run the query blocks.
+//
+// Validation (the lists the block-mask kernel writes always pass): every
+// entry in [0, nkb), no repeated entry, ascending order, and a count in
+// [0, width].  The kernels that read lists treat a list as a set of tiles
+// whatever it holds; this check tells a caller that its lists were not in the
+// documented form.
+//
+// Row order: query blocks sorted by the median tile of their lists.  Blocks
+// whose lists sit around the same tiles then run next to each other on one
+// XCD and find those tiles in its L2; the order changes nothing in any result
+// (each query block is computed on its own).
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -50,6 +59,52 @@ hipError_t launch_check_lists(const int32_t* idx, const int32_t* cnt, int64_t ro
                               int nkb, int32_t* err_flag, hipStream_t s) {
   check_lists_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(idx, cnt, rows, width, nkb,
                                                                      err_flag);
+  return hipGetLastError();
+}
+
+// One workgroup per head: a bitonic sort in LDS of the keys
+// (median entry << 12) | query block, so equal medians keep index order
+// (nqb <= 4096; an empty row sorts last with key 4096).
+__global__ __launch_bounds__(1024) void row_order_kernel(const int32_t* __restrict__ idx,
+                                                         const int32_t* __restrict__ cnt, int nqb,
+                                                         int width, int32_t* __restrict__ order) {
+  __shared__ uint32_t key[4096];
+  const int64_t bh = blockIdx.x;
+  int P = 1;
+  while (P < nqb) P <<= 1;
+  for (int i = threadIdx.x; i < P; i += 1024) {
+    uint32_t kk = 0xffffffffu;  // padding sorts after every real key
+    if (i < nqb) {
+      const int64_t row = bh * nqb + i;
+      const int c = min(cnt[row], width);
+      uint32_t m = 4096u;
+      if (c > 0) m = (uint32_t)min(max(idx[row * width + c / 2], 0), 4095);
+      kk = (m << 12) | (uint32_t)i;
+    }
+    key[i] = kk;
+  }
+  __syncthreads();
+  for (int size = 2; size <= P; size <<= 1)
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = threadIdx.x; i < P; i += 1024) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const bool up = (i & size) == 0;
+          const uint32_t a = key[i], b = key[j];
+          if ((a > b) == up) {
+            key[i] = b;
+            key[j] = a;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  for (int i = threadIdx.x; i < nqb; i += 1024) order[bh * nqb + i] = (int32_t)(key[i] & 0xfffu);
+}
+
+hipError_t launch_row_order(const int32_t* idx, const int32_t* cnt, int64_t BH, int nqb, int width,
+                            int32_t* order, hipStream_t s) {
+  row_order_kernel<<<dim3((unsigned)BH), 1024, 0, s>>>(idx, cnt, nqb, width, order);
   return hipGetLastError();
 }
 

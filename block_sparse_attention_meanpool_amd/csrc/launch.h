@@ -18,10 +18,11 @@ hipError_t launch_block_mask(const uint8_t* cls, int64_t rows, int nkb, int32_t*
                              int km_max, int32_t* err_flag, hipStream_t s);
 // lin_ws: a linear-branch workspace after launch_linear_prepare, or NULL.
 // When given, each query's linear-branch output is added before the store.
+// order: a row order (per head, a permutation of its nb query blocks) or NULL
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                        int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
                        float scale, void* o, int o_fp32, float* lse, const void* lin_ws,
-                       hipStream_t s);
+                       const int32_t* order, hipStream_t s);
 // Linear-branch workspace: per-tile states H_j^T (bf16) and z_j (fp32), the
 // marginal bit matrix (words 32-bit words per query block), zeta_i (fp32) and
 // the gathered S_i^T (bf16), each piece 256-byte aligned.
@@ -80,7 +81,7 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
                            int N, int d, int block, int nb, const int32_t* idx, const int32_t* cnt,
                            int kmax, float scale, const void* o_s, int o_fp32, const float* lse,
                            const uint16_t* d_o, float* dq, float* dk, float* dv, void* ws,
-                           hipStream_t s);
+                           const int32_t* order, hipStream_t s);
 // the two gradient kernels for the shapes other than d = 128 with 128-token
 // blocks, given D and the column lists built by launch_attn_bwd
 hipError_t launch_attn_bwd_generic(const uint16_t* q, const uint16_t* k, const uint16_t* v,
@@ -89,7 +90,7 @@ hipError_t launch_attn_bwd_generic(const uint16_t* q, const uint16_t* k, const u
                                    const void* o_s, int o_fp32, const float* lse,
                                    const uint16_t* d_o, float* dq, float* dk, float* dv,
                                    float* Dbuf, const uint16_t* col_idx, const int32_t* col_cnt,
-                                   hipStream_t s);
+                                   const int32_t* order, hipStream_t s);
 // Linear-branch backward workspace: dS_i (bf16, laid out like the states),
 // dzeta_i (fp32), the transposed marginal bit matrix, dH_j (bf16), dz_j (fp32),
 // then three arrays laid out like the states (lo_bytes each): the states' low
@@ -132,6 +133,10 @@ hipError_t launch_tile_permute(const uint16_t* x, uint16_t* y, int64_t BH, int H
                                int X, int d, const TileShapes& ts, int inverse, hipStream_t s);
 hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uint16_t* o,
                           int64_t n_elems, hipStream_t s);
+// Row order of each head's query blocks: sorted by the median entry of their
+// lists (entry min(cnt, width) / 2; empty rows last), ties by index
+hipError_t launch_row_order(const int32_t* idx, const int32_t* cnt, int64_t BH, int nqb, int width,
+                            int32_t* order, hipStream_t s);
 // ORs SLA_FLAG_LIST_* bits into *err_flag for rows of `width`-wide lists
 // whose first cnt entries leave [0, nkb), repeat, descend, or whose count
 // lies outside [0, width]

@@ -52,4 +52,15 @@ __device__ __forceinline__ bool list_entry_used(const int32_t* __restrict__ list
   return true;
 }
 
+// Query block run by the workgroup at position pos (< nqb) of its head's
+// sequence: pos itself, or entry pos of the head's row order (a permutation of
+// the head's query blocks, as sla_row_order writes; -1 for an entry outside
+// [0, nqb), whose workgroup then does nothing).
+__device__ __forceinline__ int ordered_block(const int32_t* __restrict__ order, int64_t bh,
+                                             int nqb, int pos) {
+  if (!order) return pos;
+  const int qb = order[bh * nqb + pos];
+  return qb >= 0 && qb < nqb ? qb : -1;
+}
+
 }  // namespace sla

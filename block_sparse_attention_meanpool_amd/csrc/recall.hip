@@ -34,9 +34,10 @@ hipError_t launch_recall(const uint16_t* q, const uint16_t* k, int64_t BH, int N
   float* lse_kept = reinterpret_cast<float*>(p + lw.o_bytes + lw.lse_bytes);
   // V does not enter the LSE: K stands in for it, and O goes to the workspace.
   hipError_t e = launch_attn(q, k, k, BH, N, d, block, nb, nullptr, nullptr, nb, scale, o, 0,
-                             lse_all, nullptr, s);
+                             lse_all, nullptr, nullptr, s);
   if (e != hipSuccess) return e;
-  e = launch_attn(q, k, k, BH, N, d, block, nb, idx, cnt, kmax, scale, o, 0, lse_kept, nullptr, s);
+  e = launch_attn(q, k, k, BH, N, d, block, nb, idx, cnt, kmax, scale, o, 0, lse_kept, nullptr,
+                  nullptr, s);
   if (e != hipSuccess) return e;
   const int64_t n = BH * N;
   recall_kernel<<<dim3((unsigned)((n + 255) / 256)), 256, 0, s>>>(lse_kept, lse_all, recall, n);

@@ -33,21 +33,25 @@ __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(D == 64
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse, int seg,
-    const uint16_t* __restrict__ lin_C, const float* __restrict__ lin_zeta) {
+    const uint16_t* __restrict__ lin_C, const float* __restrict__ lin_zeta,
+    const int32_t* __restrict__ order) {
   constexpr int NT = BLK * 2;   // threads
   constexpr int CH = D / 8;     // 16-byte chunks per K row
   __shared__ __attribute__((aligned(16))) uint16_t Ks[BLK * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * BLK];
 
-  // Workgroups go round-robin to the 8 XCDs.  XCD x takes query blocks
-  // [x*seg, (x+1)*seg) of every head, heads in order: neighbouring query
-  // blocks (which share most of their kept tiles) meet in one XCD's L2, and
-  // all XCDs work on the same head at a time.
+  // Workgroups go round-robin to the 8 XCDs.  XCD x takes positions
+  // [x*seg, (x+1)*seg) of every head's query-block sequence (natural order, or
+  // a row order that puts blocks with similar tile lists next to each other),
+  // heads in order: neighbouring query blocks, which share most of their kept
+  // tiles, meet in one XCD's L2, and all XCDs work on the same head at a time.
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int64_t bh = slot / seg;
-  const int qb = xcd * seg + slot % seg;
-  if (qb >= nqb) return;
+  const int pos = xcd * seg + slot % seg;
+  if (pos >= nqb) return;
+  const int qb = ordered_block(order, bh, nqb, pos);
+  if (qb < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int64_t head_off = bh * (int64_t)N * D;
@@ -323,7 +327,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     int N, int nqb, int nkb, const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt,
     int kmax, float sl2, void* __restrict__ o, int o_fp32, float* __restrict__ lse, int seg,
-    const uint16_t* __restrict__ lin_C, const float* __restrict__ lin_zeta) {
+    const uint16_t* __restrict__ lin_C, const float* __restrict__ lin_zeta,
+    const int32_t* __restrict__ order) {
   __shared__ __attribute__((aligned(1024))) char K0[BUFB];
   __shared__ __attribute__((aligned(1024))) char V0[BUFB];
   __shared__ __attribute__((aligned(1024))) char K1[BUFB];
@@ -332,8 +337,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int64_t bh = slot / seg;
-  const int qb = xcd * seg + slot % seg;
-  if (qb >= nqb) return;
+  const int pos = xcd * seg + slot % seg;
+  if (pos >= nqb) return;
+  const int qb = ordered_block(order, bh, nqb, pos);
+  if (qb < 0) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hf = lane >> 5;
   const int64_t head_off = bh * (int64_t)N * D;
@@ -428,24 +435,25 @@ template <int D, int BLK>
 static hipError_t launch_attn_t(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH,
                                 int N, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
                                 float scale, void* o, int o_fp32, float* lse,
-                                const uint16_t* lin_C, const float* lin_zeta, hipStream_t s) {
+                                const uint16_t* lin_C, const float* lin_zeta, const int32_t* order,
+                                hipStream_t s) {
   const int seg = (nb + 7) / 8;
   dim3 grid((unsigned)(BH * seg * 8));
   if (idx)
     attn_fwd_kernel<D, BLK, true><<<grid, BLK * 2, 0, s>>>(q, k, v, N, nb, nb, idx, cnt, kmax,
                                                           scale * kLog2e, o, o_fp32, lse, seg,
-                                                          lin_C, lin_zeta);
+                                                          lin_C, lin_zeta, order);
   else
     attn_fwd_kernel<D, BLK, false><<<grid, BLK * 2, 0, s>>>(q, k, v, N, nb, nb, idx, cnt, kmax,
                                                            scale * kLog2e, o, o_fp32, lse, seg,
-                                                           lin_C, lin_zeta);
+                                                           lin_C, lin_zeta, nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t BH, int N,
                        int d, int block, int nb, const int32_t* idx, const int32_t* cnt, int kmax,
                        float scale, void* o, int o_fp32, float* lse, const void* lin_ws,
-                       hipStream_t s) {
+                       const int32_t* order, hipStream_t s) {
   const uint16_t* lin_C = nullptr;
   const float* lin_zeta = nullptr;
   if (lin_ws) {
@@ -458,20 +466,22 @@ hipError_t launch_attn(const uint16_t* q, const uint16_t* k, const uint16_t* v, 
     const dim3 grid((unsigned)(BH * seg * 8));
     if (idx)
       pipe::attn_fwd_pipe_kernel<true><<<grid, pipe::NT, 0, s>>>(
-          q, k, v, N, nb, nb, idx, cnt, kmax, scale * kLog2e, o, o_fp32, lse, seg, lin_C, lin_zeta);
+          q, k, v, N, nb, nb, idx, cnt, kmax, scale * kLog2e, o, o_fp32, lse, seg, lin_C, lin_zeta,
+          order);
     else
       pipe::attn_fwd_pipe_kernel<false><<<grid, pipe::NT, 0, s>>>(
-          q, k, v, N, nb, nb, idx, cnt, kmax, scale * kLog2e, o, o_fp32, lse, seg, lin_C, lin_zeta);
+          q, k, v, N, nb, nb, idx, cnt, kmax, scale * kLog2e, o, o_fp32, lse, seg, lin_C, lin_zeta,
+          nullptr);
     return hipGetLastError();
   }
   if (d == 128 && block == 64)
     return launch_attn_t<128, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, lin_C,
-                                  lin_zeta, s);
+                                  lin_zeta, order, s);
   if (d == 64 && block == 128)
     return launch_attn_t<64, 128>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, lin_C,
-                                  lin_zeta, s);
+                                  lin_zeta, order, s);
   return launch_attn_t<64, 64>(q, k, v, BH, N, nb, idx, cnt, kmax, scale, o, o_fp32, lse, lin_C,
-                               lin_zeta, s);
+                               lin_zeta, order, s);
 }
 
 }  // namespace sla

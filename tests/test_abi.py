@@ -121,10 +121,19 @@ def test_other_entry_points_reject_bad_arguments(mod):
     assert lib.sla_block_mask(GOOD, 1, 1, 4, 4, GOOD, GOOD, 2, GOOD, GOOD, 0, None, None) == -1
     # sparse attention
     sa = lib.sla_sparse_attn_fwd
-    assert sa(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, None, GOOD, 2, 0.125, GOOD, 1, None, None) == -1
-    assert sa(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 5, 0.125, GOOD, 1, None, None) == -1
-    assert sa(GOOD, GOOD, ODD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, 0.125, GOOD, 1, None, None) == -3
-    assert sa(GOOD, GOOD, GOOD, 1, 1, 256, 80, 64, GOOD, GOOD, 2, 0.125, GOOD, 1, None, None) == -2
+    assert sa(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, None, GOOD, 2, None, 0.125, GOOD, 1, None, None) == -1
+    assert sa(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 5, None, 0.125, GOOD, 1, None, None) == -1
+    assert sa(GOOD, GOOD, ODD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, None, 0.125, GOOD, 1, None, None) == -3
+    assert sa(GOOD, GOOD, GOOD, 1, 1, 256, 80, 64, GOOD, GOOD, 2, None, 0.125, GOOD, 1, None, None) == -2
+    # a row order must be 4-byte aligned
+    assert sa(GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, P(0x10002), 0.125, GOOD, 1, None,
+              None) == -3
+    # the row order call
+    ro = lib.sla_row_order
+    assert ro(None, GOOD, 1, 1, 4, 2, GOOD, None) == -1
+    assert ro(GOOD, GOOD, 1, 1, 4097, 2, GOOD, None) == -1
+    assert ro(GOOD, GOOD, 1, 1, 4, 0, GOOD, None) == -1
+    assert ro(GOOD, GOOD, 1, 1, 4, 2, P(0x10001), None) == -3
     # dense baseline
     assert lib.sla_dense_attn_fwd(GOOD, GOOD, GOOD, 1, 1, 0, 64, 64, 0.125, GOOD, 1, None, None) == -1
     # linear branch
@@ -142,11 +151,12 @@ def test_other_entry_points_reject_bad_arguments(mod):
     assert lp(GOOD, GOOD, 1, 1, 256, 96, 64, GOOD, GOOD, 2, GOOD, 1 << 40, None) == -2
     # fused sparse + linear
     fz = lib.sla_sparse_linear_attn_fwd
-    args = [GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, 0.125, GOOD, 1 << 40, GOOD, 0,
+    args = [GOOD, GOOD, GOOD, 1, 1, 256, 64, 64, GOOD, GOOD, 2, None, 0.125, GOOD, 1 << 40, GOOD, 0,
             None, None]
     # every call below fails validation before anything is launched
-    for pos, val, want in ((12, None, -4), (13, 16, -4), (14, None, -1), (8, None, -1),
-                           (10, 5, -1), (11, 0.0, -1), (14, ODD, -3), (6, 80, -2)):
+    for pos, val, want in ((13, None, -4), (14, 16, -4), (15, None, -1), (8, None, -1),
+                           (10, 5, -1), (12, 0.0, -1), (15, ODD, -3), (6, 80, -2),
+                           (11, P(0x10002), -3)):
         bad = list(args)
         bad[pos] = val
         assert fz(*bad) == want, (pos, val)

@@ -201,7 +201,7 @@ def test_debug_build_flags_list_arguments():
             cnt[0, 0, i] = len(entries)
         idx, cnt = idx.cuda(), cnt.cuda()
         flag(clear=True)
-        assert lib.sla_sparse_attn_fwd(P(q), P(k), P(v), B, H, N, d, b, P(idx), P(cnt), 4, 0.125,
+        assert lib.sla_sparse_attn_fwd(P(q), P(k), P(v), B, H, N, d, b, P(idx), P(cnt), 4, None, 0.125,
                                        P(o), 1, None, stream) == 0
         f_attn = flag()
         flag(clear=True)
@@ -213,3 +213,49 @@ def test_debug_build_flags_list_arguments():
     assert call([0, 3, 3]) == (sla.FLAG_LIST_REPEAT,) * 2
     assert call([9, 1]) == (sla.FLAG_LIST_RANGE | sla.FLAG_LIST_ORDER,) * 2
     say("  canonical lists leave the flag at 0; repeats, range and order set their bits")
+
+
+@pytest.mark.parametrize("d,block,N", [(128, 128, 3000), (64, 64, 1500)])
+def test_row_order_changes_only_the_schedule(d, block, N):
+    """sla_row_order sorts each head's query blocks by the median entry of
+    their lists (ties by index, empty rows last); run with that order, the
+    forward (plain and fused with the linear branch) and the backward give the
+    same bits as in the natural order."""
+    spec = Spec(311, f"order_d{d}_b{block}", B=2, H=2, N=N, d=d, block=block, kind="fourier",
+                grid=(10, 10, N // 100), mode="sla3", keep=F(1, 4), marg=F(1, 4))
+    nb = spec.nb
+    say(f"[lists] row order, d={d} block={block} N={N} (nb={nb})")
+    data = generate(spec, repairs=None, threads=1)
+    g = np.random.default_rng(17)
+    do_bits = _bf16_bits(g.standard_normal((spec.B, spec.H, N, d)).astype(np.float32))
+    q, k, v, d_o = (to_dev(x) for x in (data["q"], data["k"], data["v"], do_bits))
+    kc, km = osla.selection_counts("sla3", nb, spec.keep, spec.marg)
+    cls = sla.sla_pool_classify(q, k, block, "sla3", kc, km)
+    cls[1, 1, 2] = osla.SKIP   # one row with no critical tile: it sorts last
+    ci, cc, mi, mc = sla.sla_block_mask(cls, kc, km)
+    order = sla.sla_row_order(ci, cc)
+    torch.cuda.synchronize()
+    # the order against its definition
+    ci_np, cc_np, got = ci.cpu().numpy(), cc.cpu().numpy(), order.cpu().numpy()
+    for bb in range(spec.B):
+        for h in range(spec.H):
+            key = [(int(ci_np[bb, h, i, cc_np[bb, h, i] // 2]) if cc_np[bb, h, i] > 0 else 4096, i)
+                   for i in range(nb)]
+            want = [i for _, i in sorted(key)]
+            np.testing.assert_array_equal(got[bb, h], want)
+    assert got[1, 1, -1] == 2
+    assert not np.array_equal(got[0, 0], np.arange(nb))  # not the identity on these inputs
+
+    lin_ws = sla.sla_linear_branch_prepare(k, v, block, mi, mc)
+    outs = []
+    for ro in (None, order):
+        o_s, lse = sla.sla_sparse_attn_fwd(q, k, v, block, ci, cc, o_fp32=True, want_lse=True,
+                                           row_order=ro)
+        fused, _ = sla.sla_sparse_linear_attn_fwd(q, k, v, block, ci, cc, lin_ws, o_fp32=True,
+                                                  row_order=ro)
+        dq, dk, dv = sla.sla_sparse_attn_bwd(q, k, v, block, ci, cc, o_s, lse, d_o, row_order=ro)
+        torch.cuda.synchronize()
+        outs.append([t.cpu().numpy() for t in (o_s, lse, fused, dq, dk, dv)])
+    for a, b, n in zip(outs[0], outs[1], ("O_s", "LSE", "O fused", "dQ", "dK", "dV")):
+        np.testing.assert_array_equal(a, b, err_msg=f"{n} with and without the row order")
+    say("  the order sorts by median tile; every output identical with and without it")
