@@ -6,8 +6,9 @@ include/sla.h); this package is its Python binding.
 
 from .binding import (CLS_CRITICAL, CLS_MARGINAL, CLS_SKIP, EXPORTS, FLAG_BAD_CLASS, FLAG_OVERFLOW,
                       LIB_PATH, MODES, SlaAttention, SlaError, count_from_fraction, counts_for,
-                      debug_flag_address, sla_check_lists, sla_row_order, FLAG_LIST_RANGE, FLAG_LIST_REPEAT,
-                      FLAG_LIST_ORDER, FLAG_LIST_COUNT,
+                      debug_flag_address, sla_check_lists, sla_check_row_order, sla_row_order,
+                      FLAG_LIST_RANGE, FLAG_LIST_REPEAT, FLAG_LIST_ORDER, FLAG_LIST_COUNT,
+                      FLAG_ORDER_PERM,
                       forward, lib, num_blocks, sla_attention, sla_block_mask, sla_combine,
                       sla_dense_attn_fwd, sla_linear_branch_bwd, sla_linear_branch_fwd,
                       sla_linear_branch_prepare, sla_mask_recall, sla_pool_classify,
@@ -17,8 +18,9 @@ from .binding import (CLS_CRITICAL, CLS_MARGINAL, CLS_SKIP, EXPORTS, FLAG_BAD_CL
 
 __all__ = ["CLS_CRITICAL", "CLS_MARGINAL", "CLS_SKIP", "EXPORTS", "FLAG_BAD_CLASS", "FLAG_OVERFLOW",
            "LIB_PATH", "MODES", "SlaAttention", "SlaError", "count_from_fraction", "counts_for",
-           "debug_flag_address", "sla_check_lists", "sla_row_order", "FLAG_LIST_RANGE", "FLAG_LIST_REPEAT",
-           "FLAG_LIST_ORDER", "FLAG_LIST_COUNT",
+           "debug_flag_address", "sla_check_lists", "sla_check_row_order", "sla_row_order",
+           "FLAG_LIST_RANGE", "FLAG_LIST_REPEAT", "FLAG_LIST_ORDER", "FLAG_LIST_COUNT",
+           "FLAG_ORDER_PERM",
            "forward", "lib", "num_blocks", "sla_attention", "sla_block_mask", "sla_combine",
            "sla_dense_attn_fwd", "sla_linear_branch_bwd", "sla_linear_branch_fwd",
            "sla_linear_branch_prepare", "sla_mask_recall", "sla_pool_classify",

@@ -24,6 +24,7 @@ MODES = {"topk": SEL_TOPK, "cdf": SEL_CDF, "sla3": SEL_SLA3}
 CLS_SKIP, CLS_MARGINAL, CLS_CRITICAL = 0, 1, 2
 FLAG_BAD_CLASS, FLAG_OVERFLOW = 1, 2
 FLAG_LIST_RANGE, FLAG_LIST_REPEAT, FLAG_LIST_ORDER, FLAG_LIST_COUNT = 4, 8, 16, 32
+FLAG_ORDER_PERM = 64
 
 _lib = None
 
@@ -63,6 +64,7 @@ _SIGS = {
     "sla_tile_permute": (_I32, [_P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I32, _P, _I32, _P]),
     "sla_dense_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _F, _P, _I32, _P, _P]),
     "sla_check_lists": (_I32, [_P, _P, _I64, _I32, _I64, _P, _P]),
+    "sla_check_row_order": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
     "sla_row_order": (_I32, [_P, _P, _I64, _I64, _I64, _I32, _P, _P]),
     "sla_debug_flag": (_P, []),
     "sla_status_string": (ctypes.c_char_p, [_I32]),
@@ -486,6 +488,22 @@ def sla_check_lists(idx, cnt, nkb, err_flag=None, stream=None):
     rows = idx.numel() // idx.shape[-1]
     _call("sla_check_lists", _ptr(idx), _ptr(cnt), rows, idx.shape[-1], int(nkb), _ptr(err_flag),
           _stream(stream))
+    return err_flag
+
+
+def sla_check_row_order(order, err_flag=None, stream=None):
+    """OR FLAG_ORDER_PERM into err_flag (device int32 [1], zeroed here when not
+    given) when some head's row order (int32 [B, H, nqb]) is not a permutation
+    of its query blocks; returns err_flag."""
+    if not isinstance(order, torch.Tensor) or order.dim() != 3:
+        got = tuple(order.shape) if isinstance(order, torch.Tensor) else type(order).__name__
+        raise ValueError(f"order must have shape [B, H, nqb], got {got}")
+    B, H, nqb = tuple(order.shape)
+    _dev(order, torch.int32, "order")
+    if err_flag is None:
+        err_flag = torch.zeros(1, dtype=torch.int32, device=order.device)
+    _dev(err_flag, torch.int32, "err_flag", order.device)
+    _call("sla_check_row_order", _ptr(order), B, H, nqb, _ptr(err_flag), _stream(stream))
     return err_flag
 
 

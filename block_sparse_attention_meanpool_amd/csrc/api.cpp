@@ -100,7 +100,22 @@ sla_status debug_check_lists(const int32_t* idx, const int32_t* cnt, int64_t row
     const sla_status dbg_ = debug_check_lists(idx, cnt, rows, width, nkb, stream); \
     if (dbg_ != SLA_OK) return dbg_;                                                \
   } while (0)
+sla_status debug_check_order(const int32_t* order, int64_t BH, int64_t nqb, hipStream_t stream) {
+  if (!order) return SLA_OK;
+  int32_t* flag = nullptr;
+  sla_status st = from_hip(sla::debug_flag_ptr(&flag));
+  if (st != SLA_OK) return st;
+  return from_hip(sla::launch_check_order(order, BH, (int)nqb, flag, stream));
+}
+#define SLA_DEBUG_ORDER(order, BH, nqb, stream)                         \
+  do {                                                                 \
+    const sla_status dbg_ = debug_check_order(order, BH, nqb, stream); \
+    if (dbg_ != SLA_OK) return dbg_;                                   \
+  } while (0)
 #else
+#define SLA_DEBUG_ORDER(order, BH, nqb, stream) \
+  do {                                          \
+  } while (0)
 #define SLA_DEBUG_LISTS(idx, cnt, rows, width, nkb, stream) \
   do {                                                      \
   } while (0)
@@ -117,6 +132,15 @@ sla_status sla_row_order(const int32_t* idx, const int32_t* cnt, int64_t B, int6
   if (B * H > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
   if (!aligned4(idx) || !aligned4(cnt) || !aligned4(order)) return SLA_ERR_ALIGNMENT;
   return from_hip(sla::launch_row_order(idx, cnt, B * H, (int)nqb, width, order, stream));
+}
+
+sla_status sla_check_row_order(const int32_t* order, int64_t B, int64_t H, int64_t nqb,
+                               int32_t* err_flag, hipStream_t stream) {
+  if (!order || !err_flag) return SLA_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || nqb < 1 || nqb > kMaxBlocks) return SLA_ERR_INVALID_ARG;
+  if (B * H > UINT32_MAX) return SLA_ERR_UNSUPPORTED;
+  if (!aligned4(order) || !aligned4(err_flag)) return SLA_ERR_ALIGNMENT;
+  return from_hip(sla::launch_check_order(order, B * H, (int)nqb, err_flag, stream));
 }
 
 sla_status sla_check_lists(const int32_t* idx, const int32_t* cnt, int64_t rows, int32_t width,
@@ -227,6 +251,7 @@ sla_status sla_sparse_attn_fwd(const uint16_t* q, const uint16_t* k, const uint1
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o_s)) return SLA_ERR_ALIGNMENT;
   if (!aligned4(row_order)) return SLA_ERR_ALIGNMENT;
   SLA_DEBUG_LISTS(crit_idx, crit_cnt, B * H * nb, kc_max, nb, stream);
+  SLA_DEBUG_ORDER(row_order, B * H, nb, stream);
   return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
                                    crit_cnt, kc_max, scale, o_s, o_is_fp32 != 0, lse, nullptr,
                                    row_order, stream));
@@ -307,6 +332,7 @@ sla_status sla_sparse_linear_attn_fwd(const uint16_t* q, const uint16_t* k, cons
   if (!lin_ws || lin_ws_bytes < need || !aligned16(lin_ws)) return SLA_ERR_WORKSPACE;
   if (!aligned4(row_order)) return SLA_ERR_ALIGNMENT;
   SLA_DEBUG_LISTS(crit_idx, crit_cnt, B * H * nb, kc_max, nb, stream);
+  SLA_DEBUG_ORDER(row_order, B * H, nb, stream);
   return from_hip(sla::launch_attn(q, k, v, B * H, (int)N, (int)d, block, (int)nb, crit_idx,
                                    crit_cnt, kc_max, scale, o, o_is_fp32 != 0, lse, lin_ws,
                                    row_order, stream));
@@ -340,6 +366,7 @@ sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
   const size_t need = sla_sparse_attn_bwd_ws_bytes(B, H, N, d, block);
   if (!ws || ws_bytes < need || !aligned16(ws)) return SLA_ERR_WORKSPACE;
   SLA_DEBUG_LISTS(crit_idx, crit_cnt, BH * nb, kc_max, nb, stream);
+  SLA_DEBUG_ORDER(row_order, BH, nb, stream);
   return from_hip(sla::launch_attn_bwd(q, k, v, BH, (int)N, (int)d, block, (int)nb, crit_idx,
                                        crit_cnt, kc_max, scale, o_s, o_s_is_fp32 != 0, lse, d_o,
                                        dq, dk, dv, ws, row_order, stream));
@@ -453,6 +480,6 @@ const char* sla_status_string(sla_status status) {
   }
 }
 
-int32_t sla_version(void) { return 400; }
+int32_t sla_version(void) { return 500; }
 
 }  // extern "C"

@@ -6,7 +6,8 @@
 // entry in [0, nkb), no repeated entry, ascending order, and a count in
 // [0, width].  The kernels that read lists treat a list as a set of tiles
 // whatever it holds; this check tells a caller that its lists were not in the
-// documented form.
+// documented form.  A row order must be, per head, a permutation of the query
+// blocks; a second check tells a caller when one is not.
 //
 // Row order: query blocks sorted by the median tile of their lists.  Blocks
 // whose lists sit around the same tiles then run next to each other on one
@@ -59,6 +60,33 @@ hipError_t launch_check_lists(const int32_t* idx, const int32_t* cnt, int64_t ro
                               int nkb, int32_t* err_flag, hipStream_t s) {
   check_lists_kernel<<<dim3((unsigned)((rows + 3) / 4)), 256, 0, s>>>(idx, cnt, rows, width, nkb,
                                                                      err_flag);
+  return hipGetLastError();
+}
+
+// One workgroup per head: every entry of the head's row order in [0, nqb) and
+// none repeated, i.e. a permutation (nqb <= 4096: a 4096-bit LDS bitmap).
+__global__ __launch_bounds__(256) void check_order_kernel(const int32_t* __restrict__ order, int nqb,
+                                                          int32_t* __restrict__ err_flag) {
+  __shared__ uint32_t seen[128];
+  if (threadIdx.x < 128) seen[threadIdx.x] = 0u;
+  __syncthreads();
+  const int32_t* row = order + (int64_t)blockIdx.x * nqb;
+  bool bad = false;
+  for (int i = threadIdx.x; i < nqb; i += 256) {
+    const int v = row[i];
+    if (v < 0 || v >= nqb) {
+      bad = true;
+    } else {
+      const uint32_t bit = 1u << (v & 31);
+      if (atomicOr(&seen[v >> 5], bit) & bit) bad = true;
+    }
+  }
+  if (bad) atomicOr(err_flag, SLA_FLAG_ORDER_PERM);
+}
+
+hipError_t launch_check_order(const int32_t* order, int64_t BH, int nqb, int32_t* err_flag,
+                              hipStream_t s) {
+  check_order_kernel<<<dim3((unsigned)BH), 256, 0, s>>>(order, nqb, err_flag);
   return hipGetLastError();
 }
 

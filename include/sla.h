@@ -70,6 +70,9 @@ typedef int32_t sla_status;
 #define SLA_FLAG_LIST_REPEAT 8  /* an entry equal to an earlier one of its row     */
 #define SLA_FLAG_LIST_ORDER  16 /* an entry smaller than the one before it         */
 #define SLA_FLAG_LIST_COUNT  32 /* a count outside [0, width]                      */
+/* Bit set by sla_check_row_order (and by builds with SLA_DEBUG_CHECKS). */
+#define SLA_FLAG_ORDER_PERM  64 /* a head's row order is not a permutation of its
+                                   query blocks (an entry out of range or repeated) */
 
 /*
  * Tile lists (crit_idx/crit_cnt, marg_idx/marg_cnt) are read as SETS of key
@@ -174,7 +177,11 @@ sla_status sla_block_mask(const uint8_t* cls, int64_t B, int64_t H, int64_t nqb,
  *
  * crit_idx/crit_cnt  as written by sla_block_mask (read as sets, see above)
  * row_order int32 [B, H, nb] from sla_row_order, or NULL: the order in which
- *           the query blocks run (a scheduling hint; results are identical)
+ *           the query blocks run (a scheduling hint; results are identical).
+ *           Each head's nb entries must be a permutation of 0 .. nb-1: a block
+ *           missing from it is never computed (its outputs are left as they
+ *           were) and a repeated one is computed twice; sla_check_row_order
+ *           tells whether an order qualifies.
  * o_s       [B, H, N, d]; fp32 when o_is_fp32 != 0, else bf16 (RNE) (out)
  * lse       fp32 [B, H, N] or NULL                              (out)
  */
@@ -406,8 +413,21 @@ sla_status sla_check_lists(const int32_t* idx, const int32_t* cnt, int64_t rows,
                            int64_t nkb, int32_t* err_flag, hipStream_t stream);
 
 /*
+ * Validate a row order supplied by a caller: each of the B*H heads' nqb
+ * entries must lie in [0, nqb) and none may repeat, i.e. the head's entries
+ * form a permutation of its query blocks (what sla_row_order writes).  A head
+ * that fails ORs SLA_FLAG_ORDER_PERM into *err_flag (device int32, never
+ * cleared by the library).  The softmax calls do not check this themselves.
+ *
+ * order  int32 [B, H, nqb] (in);  nqb <= 4096
+ */
+sla_status sla_check_row_order(const int32_t* order, int64_t B, int64_t H, int64_t nqb,
+                               int32_t* err_flag, hipStream_t stream);
+
+/*
  * Builds compiled with SLA_DEBUG_CHECKS validate every list argument as
- * sla_check_lists does, before each call that reads lists, into a flag word
+ * sla_check_lists does, and every row order given to a softmax call as
+ * sla_check_row_order does, before each call that reads them, into a flag word
  * the library keeps on each device; this returns that word's device address
  * on the current device (read it and clear it with ordinary copies).  NULL in
  * builds without SLA_DEBUG_CHECKS.

@@ -208,6 +208,14 @@ def test_list_validation_and_debug_flag_reject_bad_arguments(mod):
     assert cl(GOOD, GOOD, 0, 2, 8, GOOD, None) == -1
     assert cl(GOOD, GOOD, 4, 2, 4097, GOOD, None) == -1
     assert cl(GOOD, P(0x10002), 4, 2, 8, GOOD, None) == -3
+    co = lib.sla_check_row_order
+    assert co(None, 1, 1, 8, GOOD, None) == -1
+    assert co(GOOD, 1, 1, 8, None, None) == -1
+    assert co(GOOD, 0, 1, 8, GOOD, None) == -1
+    assert co(GOOD, 1, 1, 0, GOOD, None) == -1
+    assert co(GOOD, 1, 1, 4097, GOOD, None) == -1
+    assert co(P(0x10002), 1, 1, 8, GOOD, None) == -3
+    assert co(GOOD, 1, 1, 8, P(0x10001), None) == -3
     # the release build keeps no debug flag
     if os.path.abspath(mod.LIB_PATH) == os.path.join(ROOT, "block_sparse_attention_meanpool_amd",
                                                      "libsla.so"):
@@ -275,6 +283,7 @@ def test_wrappers_reject_mismatched_shapes_before_any_device_use(mod):
         lambda: mod.sla_tile_permute(q, (3, 10, 10), [(1, 8, 8)] * H, b, y=bf(B, H, N, d + 8)),
         lambda: mod.sla_combine(f32(B, H, N, d), f32(B, H, N, d + 8)),
         lambda: mod.sla_check_lists(ci, i32(B, H, nb + 1), nb),
+        lambda: mod.sla_check_row_order(i32(B, H)),
     ]
     for i, case in enumerate(cases):
         with pytest.raises(ValueError, match="shape") as e:

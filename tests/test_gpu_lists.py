@@ -9,7 +9,8 @@ its first position.  So:
   * a shuffled list gives the same set (a different summation order in the
     softmax branch): within the bars of the oracle evaluated on the class map
     of that set, and the same bits in the linear branch;
-  * sla_check_lists flags each kind of violation with its bit, and the debug
+  * sla_check_lists flags each kind of violation with its bit,
+    sla_check_row_order flags row orders that are not permutations, and the debug
     build (SLA_DEBUG_CHECKS) flags them on every call that reads lists.
 """
 
@@ -154,6 +155,32 @@ def test_check_lists_flags():
     assert got == want
 
 
+def test_check_row_order_flags():
+    """sla_check_row_order sets FLAG_ORDER_PERM exactly for the heads whose
+    entries are not a permutation of their query blocks."""
+    g = np.random.default_rng(5)
+    cases = []
+    for nqb in (1, 7, 591, 4096):
+        perm = np.stack([g.permutation(nqb) for _ in range(4)]).astype(np.int32).reshape(2, 2, nqb)
+        cases.append((f"permutations, nqb={nqb}", perm, 0))
+        if nqb > 1:
+            rep = perm.copy()
+            rep[1, 0, nqb // 2] = rep[1, 0, 0]          # one repeat, one block missing
+            cases.append((f"repeat, nqb={nqb}", rep, sla.FLAG_ORDER_PERM))
+        for bad in (nqb, -1):
+            oob = perm.copy()
+            oob[0, 1, nqb - 1] = bad
+            cases.append((f"entry {bad}, nqb={nqb}", oob, sla.FLAG_ORDER_PERM))
+    say(f"[lists] sla_check_row_order on {len(cases)} orders")
+    for what, order, want in cases:
+        got = int(sla.sla_check_row_order(torch.from_numpy(order).cuda()).item())
+        assert got == want, (what, got, want)
+    # what sla_row_order writes always passes
+    ci = torch.from_numpy(g.integers(0, 50, (2, 3, 50, 4)).astype(np.int32)).cuda()
+    cc = torch.from_numpy(g.integers(0, 5, (2, 3, 50)).astype(np.int32)).cuda()
+    assert int(sla.sla_check_row_order(sla.sla_row_order(ci, cc)).item()) == 0
+
+
 def test_debug_build_flags_list_arguments():
     """The SLA_DEBUG_CHECKS build validates the lists of every call that reads
     them into its device flag; a canonical list leaves it at zero."""
@@ -213,6 +240,20 @@ def test_debug_build_flags_list_arguments():
     assert call([0, 3, 3]) == (sla.FLAG_LIST_REPEAT,) * 2
     assert call([9, 1]) == (sla.FLAG_LIST_RANGE | sla.FLAG_LIST_ORDER,) * 2
     say("  canonical lists leave the flag at 0; repeats, range and order set their bits")
+
+    # a row order given to the softmax call is checked as well (a repeated
+    # entry: one block computed twice with the same result, one not at all)
+    idx = torch.full((B, H, nb, 4), -1, dtype=torch.int32)
+    idx[..., 0] = 0
+    cnt = torch.ones((B, H, nb), dtype=torch.int32)
+    idx, cnt = idx.cuda(), cnt.cuda()
+    for order, want in ((list(range(nb))[::-1], 0), ([0, 1, 2, 3, 4, 5, 6, 0], sla.FLAG_ORDER_PERM)):
+        ro = torch.tensor(order, dtype=torch.int32, device="cuda").view(B, H, nb)
+        flag(clear=True)
+        assert lib.sla_sparse_attn_fwd(P(q), P(k), P(v), B, H, N, d, b, P(idx), P(cnt), 4, P(ro),
+                                       0.125, P(o), 1, None, stream) == 0
+        assert flag() == want, (order, want)
+    say("  a permutation as row order leaves the flag at 0; a repeat sets FLAG_ORDER_PERM")
 
 
 @pytest.mark.parametrize("d,block,N", [(128, 128, 3000), (64, 64, 1500)])
