@@ -155,3 +155,64 @@ def backward(q, k, v, cls, b, d_o, scale=None, branches=("softmax", "linear")):
                     np.add.at(dk[bi, h], toks, ck)
                     np.add.at(dv[bi, h], toks, cv)
     return dq, dk, dv
+
+
+def backward_query_blocks(q, k, v, cls, b, d_o, blocks, scale=None,
+                          branches=("softmax", "linear")):
+    """dQ of the given query blocks of one head, as backward() computes them:
+    {i: float64 [rows of block i, d]}, with q, k, v, d_o [N, d] and cls
+    [nqb, nkb] of that head.  A query block's dQ depends only on its own rows
+    and lists, so each is computed on its own (for layers too long to run
+    backward() on every block)."""
+    N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    out = {}
+    for i in blocks:
+        lo, hi = sla.block_bounds(N, b, i)
+        qr, g = q[lo:hi], d_o[lo:hi]
+        acc = np.zeros((hi - lo, d))
+        if "softmax" in branches:
+            crit = np.nonzero(cls[i] == sla.CRITICAL)[0]
+            acc += attend_block_grad(qr, k, v, crit, b, scale, g)[0]
+        if "linear" in branches:
+            marg = np.nonzero(cls[i] == sla.MARGINAL)[0]
+            acc += linear_block_grad(qr, k, v, marg, b, g)[0]
+        out[i] = acc
+    return out
+
+
+def backward_key_tiles(q, k, v, cls, b, d_o, tiles, scale=None,
+                       branches=("softmax", "linear")):
+    """dK and dV of the given key tiles of one head, as backward() accumulates
+    them: {j: (dk, dv)}, each float64 [rows of tile j, d].  A tile's rows
+    receive the contribution of every query block whose critical (softmax) or
+    marginal (linear) list holds it, summed in query-block order; only those
+    query blocks are visited."""
+    N, d = q.shape
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    tiles = list(tiles)
+    bounds = {j: sla.block_bounds(N, b, j) for j in tiles}
+    out = {j: (np.zeros((hi - lo, d)), np.zeros((hi - lo, v.shape[1])))
+           for j, (lo, hi) in bounds.items()}
+    kinds = [(sla.CRITICAL, "softmax"), (sla.MARGINAL, "linear")]
+    for i in range(cls.shape[0]):
+        lo, hi = sla.block_bounds(N, b, i)
+        for cl, branch in kinds:
+            if branch not in branches or not any(cls[i, j] == cl for j in tiles):
+                continue
+            kept = np.nonzero(cls[i] == cl)[0]
+            if branch == "softmax":
+                _, toks, ck, cv = attend_block_grad(q[lo:hi], k, v, kept, b, scale, d_o[lo:hi])
+            else:
+                _, toks, ck, cv = linear_block_grad(q[lo:hi], k, v, kept, b, d_o[lo:hi])
+            for j in tiles:
+                if cls[i, j] != cl:
+                    continue
+                tlo, thi = bounds[j]
+                sel = (toks >= tlo) & (toks < thi)
+                out[j][0][toks[sel] - tlo] += ck[sel]
+                out[j][1][toks[sel] - tlo] += cv[sel]
+    return out
+

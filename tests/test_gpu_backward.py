@@ -270,3 +270,59 @@ def test_backward_workload(name, heads):
                              one(do_bits), branches=branches)
         for t, r, n in zip((dq, dk, dv), ref, ("dQ", "dK", "dV")):
             _grad_close(t[0, h].cpu().numpy(), r[0, 0], f"{n} head {h}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,heads,n_tiles", [("long_clip_95", (0, 23), 3),
+                                                ("long_clip_90", (0,), 2)])
+def test_backward_long_clip_sampled(name, heads, n_tiles):
+    """The 245,760-token layer (1920 blocks per head), both branches, in the
+    launch configuration the benchmark times (row order on): the GPU computes
+    every head; the oracle checks dQ of the first, the last and three seeded
+    query blocks and dK, dV of the last and seeded key tiles of the listed
+    heads (oracle.grad's samplers, equal to its whole backward on small
+    cases). A whole head of the oracle's backward would take minutes here."""
+    from synth import CONFIGS
+    spec = CONFIGS[name]
+    b, nb = spec.block, spec.nb
+    say(f"[backward long clip] {name}: H={spec.H} N={spec.N}, heads {heads}")
+    data = generate(spec)
+    g = np.random.default_rng(37)
+    do_bits = _bf16_bits(g.standard_normal((spec.B, spec.H, spec.N, spec.d), dtype=np.float32))
+    q, k, v, d_o = (to_dev(x) for x in (data["q"], data["k"], data["v"], do_bits))
+    kc, km = osla.selection_counts("sla3", nb, spec.keep, spec.marg)
+    cls = sla.sla_pool_classify(q, k, b, "sla3", kc, km)
+    ci, cc, mi, mc = sla.sla_block_mask(cls, kc, km)
+    order = sla.sla_row_order(ci, cc)
+    o_s, lse = sla.sla_sparse_attn_fwd(q, k, v, b, ci, cc, o_fp32=True, want_lse=True,
+                                       row_order=order)
+    dq, dk, dv = sla.sla_sparse_attn_bwd(q, k, v, b, ci, cc, o_s, lse, d_o, row_order=order)
+    lin_ws = sla.sla_linear_branch_prepare(k, v, b, mi, mc)
+    sla.sla_linear_branch_bwd(q, k, v, b, mi, mc, d_o, lin_ws, dq, dk, dv)
+    torch.cuda.synchronize()
+    del o_s, lse, lin_ws
+    cls_np = cls.cpu().numpy()
+    got = {n: [] for n in ("dQ", "dK", "dV")}
+    want = {n: [] for n in ("dQ", "dK", "dV")}
+    for h in heads:
+        blocks = sorted({0, nb - 1, *(int(x) for x in g.integers(1, nb - 1, 3))})
+        tiles = sorted({nb - 1, *(int(x) for x in g.integers(1, nb - 1, n_tiles - 1))})
+        one = lambda x: osla.bf16_to_f64(x[0, h])
+        args = (one(data["q"]), one(data["k"]), one(data["v"]), cls_np[0, h], b, one(do_bits))
+        rows = ograd.backward_query_blocks(*args, blocks)
+        cols = ograd.backward_key_tiles(*args, tiles)
+        gq, gk, gv = (t[0, h].cpu().numpy() for t in (dq, dk, dv))
+        for i in blocks:
+            lo, hi = osla.block_bounds(spec.N, b, i)
+            got["dQ"].append(gq[lo:hi])
+            want["dQ"].append(rows[i])
+        for j in tiles:
+            lo, hi = osla.block_bounds(spec.N, b, j)
+            got["dK"].append(gk[lo:hi])
+            want["dK"].append(cols[j][0])
+            got["dV"].append(gv[lo:hi])
+            want["dV"].append(cols[j][1])
+        say(f"  head {h}: query blocks {blocks}, key tiles {tiles} "
+            f"(listed by {[int((cls_np[0, h, :, j] > 0).sum()) for j in tiles]} query blocks)")
+    for n in ("dQ", "dK", "dV"):
+        _grad_close(np.concatenate(got[n]), np.concatenate(want[n]), f"{n} (sampled)")

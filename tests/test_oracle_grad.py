@@ -154,3 +154,29 @@ def test_linear_dq_scale_bounds_and_closed_form():
         / w[:, None] * grad.dphi(q1[0, 0])
     assert np.allclose(sc1[0, 0], want, rtol=1e-12, atol=0)
     assert np.abs(dq1).max() < 1e-12 * sc1.max()
+
+
+@pytest.mark.parametrize("branches", [("softmax",), ("linear",), ("softmax", "linear")])
+def test_sampled_gradients_equal_backward(branches):
+    """backward_query_blocks and backward_key_tiles (the samplers used on layers
+    too long for backward()) give exactly backward()'s rows: the same
+    per-block gradients summed in the same order."""
+    q, k, v, d_o, cls, b = _case(11, B=1, H=2, N=301, d=8, b=32)
+    nb = sla.num_blocks(301, b)
+    cls[0, 0, :, 4] = sla.SKIP             # a key tile no query block lists
+    ref = grad.backward(q, k, v, cls, b, d_o, branches=branches)
+    for h in range(2):
+        one = lambda x: x[0, h]
+        rows = grad.backward_query_blocks(one(q), one(k), one(v), cls[0, h], b, one(d_o),
+                                          range(nb), branches=branches)
+        tiles = grad.backward_key_tiles(one(q), one(k), one(v), cls[0, h], b, one(d_o),
+                                        [nb - 1, 0, 4, 5], branches=branches)
+        for i, got in rows.items():
+            lo, hi = sla.block_bounds(301, b, i)
+            np.testing.assert_array_equal(got, ref[0][0, h, lo:hi])
+        for j, (dk, dv) in tiles.items():
+            lo, hi = sla.block_bounds(301, b, j)
+            np.testing.assert_array_equal(dk, ref[1][0, h, lo:hi])
+            np.testing.assert_array_equal(dv, ref[2][0, h, lo:hi])
+        if h == 0:  # the tile no query block lists receives nothing
+            assert not tiles[4][0].any() and not tiles[4][1].any()
