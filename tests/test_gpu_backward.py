@@ -239,7 +239,7 @@ def test_both_branches_backward():
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,heads", [("tiny", (0, 1)), ("short_video", (0, 11)),
-                                        ("wan1p3b", (0, 7)), ("wan14b", (13,))])
+                                        ("wan1p3b", (0, 3, 7, 11)), ("wan14b", (0, 13, 39))])
 def test_backward_workload(name, heads):
     """Full-size workloads: the GPU computes every head; the oracle checks the
     listed heads in full (all of their dQ, dK, dV)."""
