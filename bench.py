@@ -19,9 +19,14 @@ Printed JSON line:
                the bf16 dense MFMA peak; traffic = HBM bytes per launch from
                the committed counter summary of the same kernel source, else
                null;
-  cpu_baseline the fp64 oracle on the host cores on a bounded sample;
+  cpu_baseline the fp64 oracle on the host cores on a bounded sample, and
+               (parity) the GPU's class map and bf16 output on those sampled
+               heads and query blocks compared with it;
   extra        per-stage times, dense baselines (this library's dense kernel
-               and torch SDPA) and ms/layer ratios.
+               and torch SDPA) and ms/layer ratios, the inputs' SHA-256, the
+               shader clock during the attention kernel (a probe wave on a
+               second stream), and the pool + classify stage's HBM bytes and
+               GB/s from its committed counter summary.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--config wan14b]
                 [--no-cpu-baseline] [--no-dense] [--profile] [--unfused]
@@ -91,6 +96,43 @@ def kernel_source_hash():
         with open(os.path.join(ROOT, "block_sparse_attention_meanpool_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
+
+
+POOL_SOURCES = ["pool_classify.hip", "common.h"]
+
+
+def pool_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in POOL_SOURCES:
+        with open(os.path.join(ROOT, "block_sparse_attention_meanpool_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _profile_fields(config_name):
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_attn_{config_name}.md")
+    fields = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            for line in fh:
+                if line.startswith("- ") and ": " in line:
+                    key, val = line[2:].split(": ", 1)
+                    fields[key.strip()] = val.strip().strip("`")
+    return fields
+
+
+def measured_pool_traffic(config_name):
+    """HBM bytes per step of the pool + score + select kernels from the committed
+    counter summary, or None when there is none or their sources have changed."""
+    fields = _profile_fields(config_name)
+    if fields.get("pool classify source sha256") != pool_source_hash():
+        return None
+    try:
+        return {"fetch": float(fields["pool classify fetch bytes per step"]),
+                "write": float(fields["pool classify write bytes per step"])}
+    except (KeyError, ValueError):
+        return None
 
 
 def measured_traffic(config_name):
@@ -182,8 +224,13 @@ def describe(spec, kc, km):
             f"block={spec.block}, {sel}")
 
 
-def cpu_baseline(spec, data, kc, km, budget_s=20.0):
-    """Time the fp64 oracle on a bounded sample of the workload on the host cores."""
+def cpu_baseline(spec, data, kc, km, budget_s=20.0, gpu=None):
+    """Time the fp64 oracle on a bounded sample of the workload on the host cores.
+
+    With `gpu` = (class map uint8 [B, H, nb, nb], bf16 output bits uint16 [B, H, N, d]) of the
+    timed run, the sampled oracle rows are also compared with the GPU's: the class map of every
+    sampled head bit for bit, and the output of every sampled query block (max-abs and rel-L2 of
+    the bf16 output against the fp64 one)."""
     from oracle import sla as osla
     try:
         from threadpoolctl import threadpool_info
@@ -196,21 +243,35 @@ def cpu_baseline(spec, data, kc, km, budget_s=20.0):
     t0 = time.perf_counter()
     g = np.random.default_rng(0)
     h = 0
-    while time.perf_counter() - t0 < budget_s and h < spec.H:
+    cmp = {"cls_mismatch": 0, "err2": 0.0, "ref2": 0.0, "max_abs": 0.0}
+    check = 0.0
+    while time.perf_counter() - t0 - check < budget_s and h < spec.H:
         q = osla.bf16_to_f64(data["q"][0, h])[None, None]
         k = osla.bf16_to_f64(data["k"][0, h])[None, None]
         v = osla.bf16_to_f64(data["v"][0, h])[None, None]
         cls, *_ = osla.class_map(q, k, spec.block, sel, spec.keep, spec.marg, spec.thr)
         rows = [(0, 0, int(i)) for i in g.choice(spec.nb, size=min(spec.nb, 128), replace=False)]
-        osla.forward_rows(q, k, v, cls, spec.block, rows)
+        res = osla.forward_rows(q, k, v, cls, spec.block, rows)
         for (_, _, i) in rows:
             lo, hi = osla.block_bounds(spec.N, spec.block, i)
             for j in np.nonzero(cls[0, 0, i] == osla.CRITICAL)[0]:
                 klo, khi = osla.block_bounds(spec.N, spec.block, int(j))
                 flop += 4.0 * (hi - lo) * (khi - klo) * spec.d
         blocks += len(rows)
+        if gpu is not None:   # outside the timed work: compare with the GPU's rows
+            t1 = time.perf_counter()
+            g_cls, g_o = gpu
+            cmp["cls_mismatch"] += int((g_cls[0, h] != cls[0, 0]).sum())
+            for (_, _, i) in rows:
+                lo, hi = osla.block_bounds(spec.N, spec.block, i)
+                got = osla.bf16_to_f64(g_o[0, h, lo:hi])
+                ref = res[(0, 0, i)][3]
+                cmp["err2"] += float(((got - ref) ** 2).sum())
+                cmp["ref2"] += float((ref ** 2).sum())
+                cmp["max_abs"] = max(cmp["max_abs"], float(np.abs(got - ref).max()))
+            check += time.perf_counter() - t1
         h += 1
-    dt = time.perf_counter() - t0
+    dt = time.perf_counter() - t0 - check
     single = None
     if spec.N * spec.H <= 4096:
         # a workload small enough for the whole oracle forward on one BLAS thread
@@ -228,6 +289,14 @@ def cpu_baseline(spec, data, kc, km, budget_s=20.0):
                        f"({dt:.1f} s)")}
     if single is not None:
         out["single_core_full_forward_s"] = single
+    if gpu is not None:
+        out["parity"] = {
+            "heads": h, "query_blocks": blocks,
+            "class_map_mismatches": cmp["cls_mismatch"],
+            "o_bf16_max_abs": cmp["max_abs"],
+            "o_bf16_rel_l2": (cmp["err2"] / cmp["ref2"]) ** 0.5 if cmp["ref2"] > 0 else 0.0,
+            "what": "GPU class map of the sampled heads vs the oracle's (bit-exact expected); "
+                    "GPU bf16 output of the sampled query blocks vs the fp64 oracle"}
     return out
 
 
@@ -277,6 +346,9 @@ def main():
     t0 = time.time()
     data = generate(spec)
     log(f"[bench] generated inputs in {time.time() - t0:.1f} s")
+    import hashlib
+    input_sha = {t: hashlib.sha256(np.ascontiguousarray(data[t]).tobytes()).hexdigest()
+                 for t in "qkv"}
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(data[t].view(np.int16)).view(torch.bfloat16).to(dev) for t in "qkv")
     torch.cuda.synchronize()
@@ -362,6 +434,28 @@ def main():
     stage_min = {s: float(np.min(ev[s])) for s in stages}
     stage_med = {s: float(np.median(ev[s])) for s in stages}
     log(f"[bench] timed {args.steps} steps: {ms_step:.3f} ms/step; stages {stage_ms}")
+    # The attention kernel's shader clock: the probe waits on a second stream
+    # while a few more launches of the kernel run (outside the timed steps).
+    def attn_only():
+        if fused:
+            sla.sla_sparse_linear_attn_fwd(q, k, v, b, crit_idx, crit_cnt, lin_ws, o=o,
+                                           row_order=order)
+        else:
+            sla.sla_sparse_attn_fwd(q, k, v, b, crit_idx, crit_cnt,
+                                    o_s=o_s if km else o, row_order=order)
+    attn_ms = stage_ms["sparse_attn"]
+    n_clk = max(3, min(20, int(200.0 / max(attn_ms, 1e-3))))
+    side = torch.cuda.Stream()
+    probe, fixed_hz = sla.sla_clock_probe(int(min(0.8 * n_clk * attn_ms * 1e3, 1e6)), stream=side)
+    for _ in range(n_clk):
+        attn_only()
+    torch.cuda.synchronize()
+    attn_sclk = sla.probe_clock_hz(probe, fixed_hz) / 1e9
+    log(f"[bench] shader clock during the attention kernel: {attn_sclk:.3f} GHz")
+    # the timed run's class map and output, for the oracle comparison of the CPU-baseline leg
+    gpu_result = None
+    if not args.no_cpu_baseline:
+        gpu_result = (cls.cpu().numpy(), o.cpu().view(torch.int16).numpy().view(np.uint16))
 
     if args.profile:
         # a plain 1 GiB device copy, the reference for scaling HBM counters
@@ -394,6 +488,8 @@ def main():
     extra = {
         "stage_ms_mean": stage_ms, "stage_ms_median": stage_med, "stage_ms_min": stage_min,
         "kept_fraction": kept_frac, "kept_flop_per_step": flop,
+        "input_sha256": input_sha,
+        "attn_sclk_ghz": attn_sclk,
         "sparse_kernel_tflops": achieved,
         "pool_classify_gbs_algorithmic": pool_bytes / (stage_ms["pool_classify"] * 1e-3) / 1e9,
     }
@@ -468,6 +564,11 @@ def main():
         extra["speedup_vs_best_dense"] = best_dense / ms_step
         log(f"[bench] dense: ours {extra['dense_kernel_ms']:.2f} ms, sdpa {extra.get('torch_sdpa_ms')}")
 
+    pool_traffic = measured_pool_traffic(spec.name)
+    if pool_traffic is not None:
+        extra["pool_classify_hbm_bytes_per_step"] = pool_traffic
+        extra["pool_classify_gbs_counted"] = ((pool_traffic["fetch"] + pool_traffic["write"]) /
+                                              (stage_ms["pool_classify"] * 1e-3) / 1e9)
     traffic = measured_traffic(spec.name)
     if traffic is not None:
         extra["attn_hbm_bytes_per_launch"] = traffic
@@ -487,7 +588,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host cores")
-        result["cpu_baseline"] = cpu_baseline(spec, data, kc, km)
+        result["cpu_baseline"] = cpu_baseline(spec, data, kc, km, gpu=gpu_result)
     print(json.dumps(result), flush=True)
 
 

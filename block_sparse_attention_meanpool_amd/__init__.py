@@ -7,6 +7,7 @@ include/sla.h); this package is its Python binding.
 from .binding import (CLS_CRITICAL, CLS_MARGINAL, CLS_SKIP, EXPORTS, FLAG_BAD_CLASS, FLAG_OVERFLOW,
                       LIB_PATH, MODES, SlaAttention, SlaError, count_from_fraction, counts_for,
                       debug_flag_address, sla_check_lists, sla_check_row_order, sla_row_order,
+                      sla_clock_probe, probe_clock_hz,
                       FLAG_LIST_RANGE, FLAG_LIST_REPEAT, FLAG_LIST_ORDER, FLAG_LIST_COUNT,
                       FLAG_ORDER_PERM,
                       forward, lib, num_blocks, sla_attention, sla_block_mask, sla_combine,
@@ -19,6 +20,7 @@ from .binding import (CLS_CRITICAL, CLS_MARGINAL, CLS_SKIP, EXPORTS, FLAG_BAD_CL
 __all__ = ["CLS_CRITICAL", "CLS_MARGINAL", "CLS_SKIP", "EXPORTS", "FLAG_BAD_CLASS", "FLAG_OVERFLOW",
            "LIB_PATH", "MODES", "SlaAttention", "SlaError", "count_from_fraction", "counts_for",
            "debug_flag_address", "sla_check_lists", "sla_check_row_order", "sla_row_order",
+           "sla_clock_probe", "probe_clock_hz",
            "FLAG_LIST_RANGE", "FLAG_LIST_REPEAT", "FLAG_LIST_ORDER", "FLAG_LIST_COUNT",
            "FLAG_ORDER_PERM",
            "forward", "lib", "num_blocks", "sla_attention", "sla_block_mask", "sla_combine",

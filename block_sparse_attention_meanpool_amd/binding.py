@@ -65,6 +65,7 @@ _SIGS = {
     "sla_dense_attn_fwd": (_I32, [_P, _P, _P, _I64, _I64, _I64, _I64, _I32, _F, _P, _I32, _P, _P]),
     "sla_check_lists": (_I32, [_P, _P, _I64, _I32, _I64, _P, _P]),
     "sla_check_row_order": (_I32, [_P, _I64, _I64, _I64, _P, _P]),
+    "sla_clock_probe": (_I32, [_P, _I32, _P, _P]),
     "sla_row_order": (_I32, [_P, _P, _I64, _I64, _I64, _I32, _P, _P]),
     "sla_debug_flag": (_P, []),
     "sla_status_string": (ctypes.c_char_p, [_I32]),
@@ -521,6 +522,28 @@ def sla_row_order(idx, cnt, order=None, stream=None):
     _dev(order, torch.int32, "order", idx.device)
     _call("sla_row_order", _ptr(idx), _ptr(cnt), B, H, nqb, width, _ptr(order), _stream(stream))
     return order
+
+
+def sla_clock_probe(span_us, out=None, stream=None):
+    """Launch the shader-clock probe on `stream` (a second stream beside the work to
+    measure): it waits span_us microseconds of the fixed-rate counter.  Returns
+    (out, fixed_hz); after a synchronize, probe_clock_hz(out, fixed_hz) is the
+    clock the chip ran at meanwhile."""
+    if out is None:
+        out = torch.zeros(4, dtype=torch.int64, device="cuda")
+    _shape(out, (4,), "out")
+    _dev(out, torch.int64, "out")
+    hz = ctypes.c_int64(0)
+    _call("sla_clock_probe", _ptr(out), int(span_us),
+          ctypes.cast(ctypes.pointer(hz), ctypes.c_void_p), _stream(stream))
+    return out, hz.value
+
+
+def probe_clock_hz(out, fixed_hz):
+    """Shader clock (Hz) from the probe's readings: counter differences times the
+    fixed rate."""
+    c0, c1, r0, r1 = (int(x) for x in out.cpu().tolist())
+    return (c1 - c0) / max(r1 - r0, 1) * fixed_hz
 
 
 def debug_flag_address():

@@ -30,7 +30,7 @@ ARCH = "gfx950"
 SOURCES = ["api.cpp", "pool_classify.hip", "block_mask.hip", "sparse_attn.hip", "linear_branch.hip",
            "attn_bwd.hip", "attn_bwd_generic.hip", "linear_bwd.hip",
            "linear_bwd_generic.hip", "recall.hip",
-           "tile_permute.hip", "noalloc.hip", "check_lists.hip"]
+           "tile_permute.hip", "noalloc.hip", "check_lists.hip", "clock_probe.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -134,6 +134,23 @@ sla_status sla_row_order(const int32_t* idx, const int32_t* cnt, int64_t B, int6
   return from_hip(sla::launch_row_order(idx, cnt, B * H, (int)nqb, width, order, stream));
 }
 
+sla_status sla_clock_probe(int64_t* out, int32_t span_us, int64_t* fixed_hz, hipStream_t stream) {
+  if (!out || !fixed_hz || span_us < 1 || span_us > 1000000) return SLA_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(out) & 7u) return SLA_ERR_ALIGNMENT;
+  int dev = -1, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+    return SLA_ERR_HIP;
+  *fixed_hz = (int64_t)khz * 1000;
+  const uint64_t ticks = (uint64_t)khz * (uint64_t)span_us / 1000u;
+  // each iteration sleeps about 4 x 64 shader cycles (~0.1 us near 2.5 GHz), so 40 per
+  // requested microsecond is well above what the span needs; the cap only ends the wait of
+  // a counter that does not advance (the readings stay consistent: the ratio uses both
+  // counters' actual differences)
+  const uint32_t max_iter = (uint32_t)span_us * 40u + 1000u;
+  return from_hip(sla::launch_clock_probe(out, ticks > 0 ? ticks : 1, max_iter, stream));
+}
+
 sla_status sla_check_row_order(const int32_t* order, int64_t B, int64_t H, int64_t nqb,
                                int32_t* err_flag, hipStream_t stream) {
   if (!order || !err_flag) return SLA_ERR_INVALID_ARG;

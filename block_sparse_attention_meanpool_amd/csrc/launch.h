@@ -135,6 +135,7 @@ hipError_t launch_combine(const void* o_s, int o_s_fp32, const float* o_lin, uin
                           int64_t n_elems, hipStream_t s);
 // Row order of each head's query blocks: sorted by the median entry of their
 // lists (entry min(cnt, width) / 2; empty rows last), ties by index
+hipError_t launch_clock_probe(int64_t* out, uint64_t ticks, uint32_t max_iter, hipStream_t s);
 hipError_t launch_check_order(const int32_t* order, int64_t BH, int nqb, int32_t* err_flag,
                               hipStream_t s);
 hipError_t launch_row_order(const int32_t* idx, const int32_t* cnt, int64_t BH, int nqb, int width,

@@ -425,6 +425,21 @@ sla_status sla_check_row_order(const int32_t* order, int64_t B, int64_t H, int64
                                int32_t* err_flag, hipStream_t stream);
 
 /*
+ * Shader-clock probe, a measurement aid: one wavefront that reads the shader
+ * clock counter and the fixed-rate counter, sleeps until the fixed-rate counter
+ * has advanced by span_us microseconds, and reads both again.  Launched on a
+ * second stream beside other work (it holds a few registers and no LDS), it
+ * measures the clock that work runs at, which the chip lowers under a heavy
+ * load:  clock = (out[1] - out[0]) / (out[3] - out[2]) * (*fixed_hz).
+ *
+ * out       device int64 [4]: shader counter at start and end, fixed-rate
+ *           counter at start and end (out; 8-byte aligned)
+ * span_us   in [1, 10^6]; the wait also ends after a bounded number of steps
+ * fixed_hz  host int64: the fixed-rate counter's frequency (out)
+ */
+sla_status sla_clock_probe(int64_t* out, int32_t span_us, int64_t* fixed_hz, hipStream_t stream);
+
+/*
  * Builds compiled with SLA_DEBUG_CHECKS validate every list argument as
  * sla_check_lists does, and every row order given to a softmax call as
  * sla_check_row_order does, before each call that reads them, into a flag word

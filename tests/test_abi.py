@@ -208,6 +208,12 @@ def test_list_validation_and_debug_flag_reject_bad_arguments(mod):
     assert cl(GOOD, GOOD, 0, 2, 8, GOOD, None) == -1
     assert cl(GOOD, GOOD, 4, 2, 4097, GOOD, None) == -1
     assert cl(GOOD, P(0x10002), 4, 2, 8, GOOD, None) == -3
+    cp = lib.sla_clock_probe
+    assert cp(None, 10, GOOD, None) == -1
+    assert cp(GOOD, 10, None, None) == -1
+    assert cp(GOOD, 0, GOOD, None) == -1
+    assert cp(GOOD, 1000001, GOOD, None) == -1
+    assert cp(P(0x10004), 10, GOOD, None) == -3
     co = lib.sla_check_row_order
     assert co(None, 1, 1, 8, GOOD, None) == -1
     assert co(GOOD, 1, 1, 8, None, None) == -1
