@@ -266,49 +266,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV, one workgroup per key tile
+// dK, dV, one workgroup per key tile, two waves per SIMD
 // ---------------------------------------------------------------------------
+// A workgroup runs the query blocks that list its key tile in list order, each
+// as four 32-query stages: S = Q K^T, dP = dO V^T, P = exp2(S sl2 - LSE log2 e),
+// dS = P (dP - D); dV^T += dO^T P, dK^T += Q^T dS.  K stays in registers; V
+// (the tile's 128 rows) sits in LDS for the dP products; Q and dO come in
+// 32-row stages through two alternating buffers chosen at run time, which
+// keeps the swizzled LDS addresses loop-variant instead of one register per
+// address.  64 KB of LDS and at most 256 registers let two workgroups share a
+// CU, so each SIMD runs two waves.
 
-// 64 query rows of Q and dO, and their LSE and D, for one half of a query block.
-__device__ __forceinline__ void issue_qhalf(const __amdgpu_buffer_rsrc_t& rq,
-                                            const __amdgpu_buffer_rsrc_t& rdo,
-                                            const __amdgpu_buffer_rsrc_t& rl,
-                                            const __amdgpu_buffer_rsrc_t& re, int row0, char* qbuf,
-                                            char* obuf, float* lbuf, float* ebuf, int lane, int w) {
-  issue_rows(rq, rdo, row0, qbuf, obuf, lane, w);
-  // The wave index is the same in every lane; taken through readfirstlane the
-  // compiler knows it, so descriptor and LDS destination stay scalar instead
-  // of being looped over lane by lane.
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const uint32_t off = (uint32_t)(row0 + lane) * 4;
-  if (wu == 0)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void_ptr)lbuf, 4, off, 0, 0, 0);
-  else if (wu == 1)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void_ptr)ebuf, 4, off, 0, 0, 0);
-}
-
-// One 64-query half: for each 32-query block, S = Q K^T, dP = dO V^T,
-// dS = P (dP - D); dV^T += dO^T P, dK^T += Q^T dS.
-// One 32-query sub-block's S = Q K^T and dP = dO V^T (K^T and V^T in registers).
-__device__ __forceinline__ void sdp_block(const char* qbuf, const char* obuf, const u32x4 (&kf)[8],
-                                          const u32x4 (&vf)[8], int qb2, int hf, int qrowp,
-                                          f32x16& sacc, f32x16& dpacc) {
-  sacc = f32x16{};
-  dpacc = f32x16{};
-#pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    sacc = mfma32x32x16(dual_row_read(qbuf, 32 * qb2 + qrowp, 2 * ks + hf), kf[ks], sacc);
-    dpacc = mfma32x32x16(dual_row_read(obuf, 32 * qb2 + qrowp, 2 * ks + hf), vf[ks], dpacc);
-  }
-}
-
-// dV += P^T dO and dK += dS^T Q over the sub-block's 32 queries.
-__device__ __forceinline__ void acc_block(const char* qbuf, const char* obuf, int qb2, int lane,
+// dV += P^T dO and dK += dS^T Q over a stage's 32 queries.
+__device__ __forceinline__ void acc_block(const char* qbuf, const char* obuf, int lane,
                                           const u32x4 (&pb)[2], const u32x4 (&dsb)[2],
                                           f32x16 (&dkacc)[4], f32x16 (&dvacc)[4]) {
 #pragma unroll
   for (int hs = 0; hs < 2; ++hs) {
-    const int k0 = 16 * (2 * qb2 + hs);
+    const int k0 = 16 * hs;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       dvacc[db] = mfma32x32x16(tr_operand<DualSwz>(obuf, k0, 32 * db, lane), pb[hs], dvacc[db]);
@@ -318,12 +293,12 @@ __device__ __forceinline__ void acc_block(const char* qbuf, const char* obuf, in
 }
 
 // One softmax step: P = exp2(S sl2 - LSE log2 e) and dS = P (dP - D) for the
-// register pair r = 8 hs + 2 p (queries 32 qb2 + 16 hs + 8 hf + 2 p and the
+// register pair r = 8 hs + 2 p (stage queries 16 hs + 8 hf + 2 p and the
 // next), packed into the bf16 B operands pb[hs] and dsb[hs].
-__device__ __forceinline__ void pds_step(const float* lbuf, const float* ebuf, int qb2, int hf,
+__device__ __forceinline__ void pds_step(const float* lbuf, const float* ebuf, int hf,
                                          float sl2, const f32x16& sacc, const f32x16& dpacc,
                                          int hs, int p, u32x4 (&pb)[2], u32x4 (&dsb)[2]) {
-  const int q0 = 32 * qb2 + 16 * hs + 8 * hf + 2 * p;
+  const int q0 = 16 * hs + 8 * hf + 2 * p;
   const f32x2 lp = *(const f32x2*)(lbuf + q0), ep = *(const f32x2*)(ebuf + q0);
   const float l0 = lp[0], l1 = lp[1], e0 = ep[0], e1 = ep[1];
   const int r = 8 * hs + 2 * p;
@@ -333,47 +308,42 @@ __device__ __forceinline__ void pds_step(const float* lbuf, const float* ebuf, i
   dsb[hs][p] = pack_bf16x2(p0 * (dpacc[r] - e0), p1 * (dpacc[r + 1] - e1));
 }
 
-// One 64-query half: two sub-blocks, software-pipelined by hand: each of the
-// second sub-block's eight S/dP steps (two MFMAs) carries one softmax step of
-// the first, and each of the first sub-block's eight dV/dK steps carries one
-// of the second.  dK and dV accumulate in the plain order.
-__device__ __forceinline__ void dkdv_half(const char* qbuf, const char* obuf, const float* lbuf,
-                                          const float* ebuf, const u32x4 (&kf)[8],
-                                          const u32x4 (&vf)[8], f32x16 (&dkacc)[4],
-                                          f32x16 (&dvacc)[4], float sl2, int hf, int qrowp,
-                                          int lane) {
-  f32x16 s0, d0, s1 = f32x16{}, d1 = f32x16{};
-  u32x4 p0[2], ds0[2], p1[2], ds1[2];
-  sdp_block(qbuf, obuf, kf, vf, 0, hf, qrowp, s0, d0);
+constexpr int SROWS = 32, SBUF = SROWS * 256;  // 8 KB per stage buffer
+
+// Rows [row0, row0 + 32) of Q and dO into a dual-swizzled stage (2 KB of each
+// per wave), and their LSE and D (wave 0 and 1, 64 entries each; the 32 past
+// the stage are never read).
+__device__ __forceinline__ void issue_stage(const __amdgpu_buffer_rsrc_t& rq,
+                                            const __amdgpu_buffer_rsrc_t& rdo,
+                                            const __amdgpu_buffer_rsrc_t& rl,
+                                            const __amdgpu_buffer_rsrc_t& re, int row0, char* qbuf,
+                                            char* obuf, float* lbuf, float* ebuf, int lane, int wu) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    s1 = mfma32x32x16(dual_row_read(qbuf, 32 + qrowp, 2 * ks + hf), kf[ks], s1);
-    d1 = mfma32x32x16(dual_row_read(obuf, 32 + qrowp, 2 * ks + hf), vf[ks], d1);
-    pds_step(lbuf, ebuf, 0, hf, sl2, s0, d0, ks >> 2, ks & 3, p0, ds0);
+  for (int e = 0; e < 2; ++e) {
+    const int inst = 2 * wu + e;
+    const int row = 4 * inst + (lane >> 4);
+    const int ch = (lane & 15) ^ dual_swz(row);
+    const uint32_t off = (uint32_t)((row0 + row) * D + ch * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_ptr)(qbuf + inst * 1024), 16, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rdo, (lds_void_ptr)(obuf + inst * 1024), 16, off, 0, 0, 0);
   }
-#pragma unroll
-  for (int hs = 0; hs < 2; ++hs)
-#pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const int k0 = 16 * hs;
-      dvacc[db] = mfma32x32x16(tr_operand<DualSwz>(obuf, k0, 32 * db, lane), p0[hs], dvacc[db]);
-      dkacc[db] = mfma32x32x16(tr_operand<DualSwz>(qbuf, k0, 32 * db, lane), ds0[hs], dkacc[db]);
-      pds_step(lbuf, ebuf, 1, hf, sl2, s1, d1, hs, db, p1, ds1);
-    }
-  acc_block(qbuf, obuf, 1, lane, p1, ds1, dkacc, dvacc);
+  const uint32_t off = (uint32_t)(row0 + lane) * 4;
+  if (wu == 0)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lds_void_ptr)lbuf, 4, off, 0, 0, 0);
+  else if (wu == 1)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(re, (lds_void_ptr)ebuf, 4, off, 0, 0, 0);
 }
 
-__global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
     const float* __restrict__ lse, const float* __restrict__ Dbuf,
     const uint16_t* __restrict__ d_o, int N, int nqb, int nkb,
     const uint16_t* __restrict__ col_idx, const int32_t* __restrict__ col_cnt, int width,
     float sl2, float scale, float* __restrict__ dk, float* __restrict__ dv, int seg) {
-  __shared__ __attribute__((aligned(1024))) char Q0[BUFB];
-  __shared__ __attribute__((aligned(1024))) char O0[BUFB];
-  __shared__ __attribute__((aligned(1024))) char Q1[BUFB];
-  __shared__ __attribute__((aligned(1024))) char O1[BUFB];
-  __shared__ __attribute__((aligned(256))) float L0[HALF], E0[HALF], L1[HALF], E1[HALF];
+  __shared__ __attribute__((aligned(1024))) char Vt[BLK * 256];
+  __shared__ __attribute__((aligned(1024))) char QS[2][SBUF];
+  __shared__ __attribute__((aligned(1024))) char OS[2][SBUF];
+  __shared__ __attribute__((aligned(256))) float LS[2][64], ES[2][64];
 
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
@@ -381,6 +351,7 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(
   const int kt = xcd * seg + slot % seg;
   if (kt >= nkb) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int l32 = lane & 31, hf = lane >> 5;
   const int64_t head_off = bh * (int64_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -392,32 +363,62 @@ __global__ __launch_bounds__(NT) void attn_bwd_dkdv_kernel(
   const __amdgpu_buffer_rsrc_t re = make_rsrc(Dbuf + bh * N, (uint32_t)N * 4);
 
   const int count = col_cnt[bh * nkb + kt];
-  const int64_t list0 = (bh * nkb + kt) * (int64_t)width;  // first entry of this tile's list
+  const int64_t list0 = (bh * nkb + kt) * (int64_t)width;
+  const int nst = 4 * count;  // stages: 4 per listed query block
+  // this tile's V rows, row-major with the K tiles' swizzle (8 KB per wave);
+  // nothing is loaded for an empty list, so no load outlives the workgroup
+  if (nst > 0)
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const int inst = 8 * wu + e;
+    const int row = 4 * inst + (lane >> 4);
+    const uint32_t off =
+        (uint32_t)((kt * BLK + row) * D + ((lane & 15) ^ row_swz<16>(row)) * 8) * 2;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_ptr)(Vt + inst * 1024), 16, off, 0, 0, 0);
+  }
   int i_cur = count > 0 ? u16_entry(col_idx, list0) : 0;
-  if (count > 0) issue_qhalf(rq, rdo, rl, re, i_cur * BLK, Q0, O0, L0, E0, lane, w);
+  if (nst > 0) issue_stage(rq, rdo, rl, re, i_cur * BLK, QS[0], OS[0], LS[0], ES[0], lane, wu);
 
   const int key = kt * BLK + 32 * w + l32;
-  u32x4 kf[8], vf[8];
+  u32x4 kf[8];
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    const uint32_t off = (uint32_t)(key * D + 16 * ks + 8 * hf) * 2;
-    kf[ks] = buf_load16(rk, off);
-    vf[ks] = buf_load16(rv, off);
-  }
+  for (int ks = 0; ks < 8; ++ks) kf[ks] = buf_load16(rk, (uint32_t)(key * D + 16 * ks + 8 * hf) * 2);
   f32x16 dkacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   f32x16 dvacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   const int qrowp = swap_bits_2_3(l32);
-  for (int t = 0; t < count; ++t) {
-    const int i_next = (t + 1 < count) ? u16_entry(col_idx, list0 + t + 1) : 0;
+  const int vrow = 32 * w + l32;
+
+#pragma unroll 1
+  for (int u = 0; u < nst; ++u) {
+    const int t = u >> 2, st = u & 3, b = u & 1;
+    int i_nx = i_cur;
+    if (st == 3) i_nx = (t + 1 < count) ? u16_entry(col_idx, list0 + t + 1) : 0;
     wait_vmcnt0();
-    __syncthreads();  // buffer 0 complete; every wave is done with buffer 1
-    issue_qhalf(rq, rdo, rl, re, i_cur * BLK + HALF, Q1, O1, L1, E1, lane, w);
-    dkdv_half(Q0, O0, L0, E0, kf, vf, dkacc, dvacc, sl2, hf, qrowp, lane);
-    wait_vmcnt0();
-    __syncthreads();  // buffer 1 complete; every wave is done with buffer 0
-    if (t + 1 < count) issue_qhalf(rq, rdo, rl, re, i_next * BLK, Q0, O0, L0, E0, lane, w);
-    if (i_cur * BLK + HALF < N) dkdv_half(Q1, O1, L1, E1, kf, vf, dkacc, dvacc, sl2, hf, qrowp, lane);
-    i_cur = i_next;
+    __syncthreads();  // stage u complete in buffer b; every wave is done with buffer b ^ 1
+    if (u + 1 < nst)
+      issue_stage(rq, rdo, rl, re, i_nx * BLK + SROWS * ((st + 1) & 3), QS[b ^ 1], OS[b ^ 1],
+                  LS[b ^ 1], ES[b ^ 1], lane, wu);
+    if (i_cur * BLK + SROWS * st < N) {
+      const char* qbuf = QS[b];
+      const char* obuf = OS[b];
+      f32x16 sacc = f32x16{}, dpacc = f32x16{};
+      // LLVM's softmax-interleave strategy for the stage (instruction order
+      // only; about 1% off the backward, same bits)
+      __builtin_amdgcn_iglp_opt(2);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        sacc = mfma32x32x16(dual_row_read(qbuf, qrowp, 2 * ks + hf), kf[ks], sacc);
+        const u32x4 vb = *(const u32x4*)(Vt + row_offset<16>(vrow, 2 * ks + hf));
+        dpacc = mfma32x32x16(dual_row_read(obuf, qrowp, 2 * ks + hf), vb, dpacc);
+      }
+      u32x4 pb[2], dsb[2];
+#pragma unroll
+      for (int hs = 0; hs < 2; ++hs)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) pds_step(LS[b], ES[b], hf, sl2, sacc, dpacc, hs, p, pb, dsb);
+      acc_block(qbuf, obuf, lane, pb, dsb, dkacc, dvacc);
+    }
+    i_cur = i_nx;
   }
 
   if (key < N) {
@@ -495,7 +496,7 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   bwd::attn_bwd_dkdv_kernel<<<grid, bwd::NT, 0, s>>>(q, k, v, lse, Dbuf, d_o, N, nb, nb, col_idx,
-                                                     col_cnt, nb, sl2, scale, dk, dv, seg);
+                                                      col_cnt, nb, sl2, scale, dk, dv, seg);
   return hipGetLastError();
 }
 
