@@ -166,7 +166,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
     const void* __restrict__ o_s, int o_fp32, const float* __restrict__ lse,
     const uint16_t* __restrict__ d_o, int N, int nqb, int nkb, const int32_t* __restrict__ idx,
     const int32_t* __restrict__ cnt, int kmax, float sl2, float scale, float* __restrict__ dq,
-    float* __restrict__ Dbuf, int seg, const int32_t* __restrict__ order) {
+    float* __restrict__ Dbuf, float* __restrict__ L2buf, int seg, const int32_t* __restrict__ order) {
   __shared__ __attribute__((aligned(1024))) char K0[BUFB];
   __shared__ __attribute__((aligned(1024))) char V0[BUFB];
   __shared__ __attribute__((aligned(1024))) char K1[BUFB];
@@ -232,7 +232,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   }
   dn = sum_halves(dn);
   const float lse2 = qrow < N ? lse[bh * N + qrow] * kLog2e : 0.f;
-  if (hf == 0 && qrow < N) Dbuf[bh * N + qrow] = dn;
+  if (hf == 0 && qrow < N) {
+    Dbuf[bh * N + qrow] = dn;
+    L2buf[bh * N + qrow] = lse2;  // LSE log2 e, as the dK/dV pass uses it
+  }
 
   f32x16 dqacc[4] = {f32x16{}, f32x16{}, f32x16{}, f32x16{}};
   const int krow = swap_bits_2_3(l32);
@@ -302,8 +305,8 @@ __device__ __forceinline__ void pds_step(const float* lbuf, const float* ebuf, i
   const f32x2 lp = *(const f32x2*)(lbuf + q0), ep = *(const f32x2*)(ebuf + q0);
   const float l0 = lp[0], l1 = lp[1], e0 = ep[0], e1 = ep[1];
   const int r = 8 * hs + 2 * p;
-  const float p0 = fast_exp2(fmaf(sacc[r], sl2, -l0 * kLog2e));
-  const float p1 = fast_exp2(fmaf(sacc[r + 1], sl2, -l1 * kLog2e));
+  const float p0 = fast_exp2(fmaf(sacc[r], sl2, -l0));
+  const float p1 = fast_exp2(fmaf(sacc[r + 1], sl2, -l1));
   pb[hs][p] = pack_bf16x2(p0, p1);
   dsb[hs][p] = pack_bf16x2(p0 * (dpacc[r] - e0), p1 * (dpacc[r + 1] - e1));
 }
@@ -311,8 +314,9 @@ __device__ __forceinline__ void pds_step(const float* lbuf, const float* ebuf, i
 constexpr int SROWS = 32, SBUF = SROWS * 256;  // 8 KB per stage buffer
 
 // Rows [row0, row0 + 32) of Q and dO into a dual-swizzled stage (2 KB of each
-// per wave), and their LSE and D (wave 0 and 1, 64 entries each; the 32 past
-// the stage are never read).
+// per wave), and their LSE log2 e and D (wave 0 and 1, 64 entries each; the 32
+// past the stage are never read).  The dQ pass writes LSE log2 e beside D, so
+// the stage's exponent is one fma.
 __device__ __forceinline__ void issue_stage(const __amdgpu_buffer_rsrc_t& rq,
                                             const __amdgpu_buffer_rsrc_t& rdo,
                                             const __amdgpu_buffer_rsrc_t& rl,
@@ -336,7 +340,7 @@ __device__ __forceinline__ void issue_stage(const __amdgpu_buffer_rsrc_t& rq,
 
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void attn_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k, const uint16_t* __restrict__ v,
-    const float* __restrict__ lse, const float* __restrict__ Dbuf,
+    const float* __restrict__ L2buf, const float* __restrict__ Dbuf,
     const uint16_t* __restrict__ d_o, int N, int nqb, int nkb,
     const uint16_t* __restrict__ col_idx, const int32_t* __restrict__ col_cnt, int width,
     float sl2, float scale, float* __restrict__ dk, float* __restrict__ dv, int seg) {
@@ -359,7 +363,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(d_o + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(L2buf + bh * N, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t re = make_rsrc(Dbuf + bh * N, (uint32_t)N * 4);
 
   const int count = col_cnt[bh * nkb + kt];
@@ -457,7 +461,7 @@ AttnBwdWs attn_bwd_ws_layout(int64_t BH, int N, int nb) {
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   AttnBwdWs w;
   w.wc = 2 * ((nb + 63) / 64);
-  w.d_bytes = up((size_t)BH * N * 4);
+  w.d_bytes = 2 * up((size_t)BH * N * 4);  // D, then LSE log2 e
   w.bits_bytes = up((size_t)BH * nb * w.wc * 4);
   w.cnt_bytes = up((size_t)BH * nb * 4);
   w.idx_bytes = up((size_t)BH * nb * nb * 2);
@@ -474,6 +478,7 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   const AttnBwdWs lw = attn_bwd_ws_layout(BH, N, nb);
   char* p = static_cast<char*>(ws);
   float* Dbuf = reinterpret_cast<float*>(p);
+  float* L2buf = reinterpret_cast<float*>(p + lw.d_bytes / 2);
   uint32_t* bitsT = reinterpret_cast<uint32_t*>(p + lw.d_bytes);
   int32_t* col_cnt = reinterpret_cast<int32_t*>(p + lw.d_bytes + lw.bits_bytes);
   uint16_t* col_idx = reinterpret_cast<uint16_t*>(p + lw.d_bytes + lw.bits_bytes + lw.cnt_bytes);
@@ -492,10 +497,10 @@ hipError_t launch_attn_bwd(const uint16_t* q, const uint16_t* k, const uint16_t*
   const dim3 grid((unsigned)(BH * seg * 8));
   const float sl2 = scale * kLog2e;
   bwd::attn_bwd_dq_kernel<<<grid, bwd::NT, 0, s>>>(q, k, v, o_s, o_fp32, lse, d_o, N, nb, nb, idx,
-                                                   cnt, kmax, sl2, scale, dq, Dbuf, seg, order);
+                                                   cnt, kmax, sl2, scale, dq, Dbuf, L2buf, seg, order);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  bwd::attn_bwd_dkdv_kernel<<<grid, bwd::NT, 0, s>>>(q, k, v, lse, Dbuf, d_o, N, nb, nb, col_idx,
+  bwd::attn_bwd_dkdv_kernel<<<grid, bwd::NT, 0, s>>>(q, k, v, L2buf, Dbuf, d_o, N, nb, nb, col_idx,
                                                       col_cnt, nb, sl2, scale, dk, dv, seg);
   return hipGetLastError();
 }

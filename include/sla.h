@@ -293,8 +293,9 @@ sla_status sla_sparse_attn_bwd(const uint16_t* q, const uint16_t* k, const uint1
                                const uint16_t* d_o, float* dq, float* dk, float* dv, void* ws,
                                size_t ws_bytes, hipStream_t stream);
 
-/* Workspace bytes for sla_sparse_attn_bwd: D (fp32 [B, H, N]) and the
- * per-key-tile query-block lists.  0 for unsupported arguments. */
+/* Workspace bytes for sla_sparse_attn_bwd: D and LSE log2 e (fp32 [B, H, N]
+ * each) and the per-key-tile query-block lists.  0 for unsupported
+ * arguments. */
 size_t sla_sparse_attn_bwd_ws_bytes(int64_t B, int64_t H, int64_t N, int64_t d, int32_t block);
 
 /*

@@ -99,10 +99,11 @@ def test_workspace_sizes(mod):
     # aligned), fp32 zeta_i [8, 128], bf16 gathered S_i^T [8, 128*128]
     assert lib.sla_linear_branch_ws_bytes(1, 1, 1000, 128, 128) == \
         8 * 128 * 128 * 2 + 8 * 128 * 4 + 256 + 8 * 128 * 4 + 8 * 128 * 128 * 2
-    # backward, every shape: D fp32 [2, 1024], column bits [2, 16, 2 words],
-    # counts [2, 16], uint16 column lists [2, 16, 16] (each piece 256-byte aligned)
+    # backward, every shape: D and LSE log2 e fp32 [2, 1024] each, column bits
+    # [2, 16, 2 words], counts [2, 16], uint16 column lists [2, 16, 16] (each piece
+    # 256-byte aligned)
     for d, b in ((64, 64), (128, 64)):
-        assert lib.sla_sparse_attn_bwd_ws_bytes(1, 2, 1024, d, b) == 8192 + 256 + 256 + 1024
+        assert lib.sla_sparse_attn_bwd_ws_bytes(1, 2, 1024, d, b) == 2 * 8192 + 256 + 256 + 1024
     # linear backward: dS_i and dH_j bf16 [2, 16, d*d], dzeta_i and dz_j fp32 [2, 16, d],
     # column bits [2, 16, 2 words], then the states' low parts and S_i as a hi + lo
     # pair, bf16 [2, 16, d*d] each
