@@ -352,7 +352,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int xcd = blockIdx.x & 7;
   const int slot = blockIdx.x >> 3;
   const int64_t bh = slot / seg;
-  const int kt = xcd * seg + slot % seg;
+  // Each XCD takes a contiguous range of a head's key tiles (their column lists
+  // overlap, which its L2 serves), and the range rotates from head to head:
+  // tiles in some positions are listed by many more query blocks than others,
+  // and a fixed range per XCD left some XCDs idle at the end.
+  const int kt = (int)((xcd + bh) & 7) * seg + slot % seg;
   if (kt >= nkb) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
