@@ -277,7 +277,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
 // (the tile's 128 rows) sits in LDS for the dP products; Q and dO come in
 // 32-row stages through two alternating buffers chosen at run time, which
 // keeps the swizzled LDS addresses loop-variant instead of one register per
-// address.  64 KB of LDS and at most 256 registers let two workgroups share a
+// address.  65 KB of LDS and at most 256 registers let two workgroups share a
 // CU, so each SIMD runs two waves.
 
 // dV += P^T dO and dK += dS^T Q over a stage's 32 queries.
@@ -375,14 +375,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
   const int nst = 4 * count;  // stages: 4 per listed query block
   // this tile's V rows, row-major with the K tiles' swizzle (8 KB per wave);
   // nothing is loaded for an empty list, so no load outlives the workgroup
-  if (nst > 0)
+  if (nst > 0) {
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int inst = 8 * wu + e;
-    const int row = 4 * inst + (lane >> 4);
-    const uint32_t off =
-        (uint32_t)((kt * BLK + row) * D + ((lane & 15) ^ row_swz<16>(row)) * 8) * 2;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_ptr)(Vt + inst * 1024), 16, off, 0, 0, 0);
+    for (int e = 0; e < 8; ++e) {
+      const int inst = 8 * wu + e;
+      const int row = 4 * inst + (lane >> 4);
+      const uint32_t off =
+          (uint32_t)((kt * BLK + row) * D + ((lane & 15) ^ row_swz<16>(row)) * 8) * 2;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_ptr)(Vt + inst * 1024), 16, off, 0, 0, 0);
+    }
   }
   int i_cur = count > 0 ? u16_entry(col_idx, list0) : 0;
   if (nst > 0) issue_stage(rq, rdo, rl, re, i_cur * BLK, QS[0], OS[0], LS[0], ES[0], lane, wu);
