@@ -411,12 +411,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2))) void
       const char* qbuf = QS[b];
       const char* obuf = OS[b];
       f32x16 sacc = f32x16{}, dpacc = f32x16{};
-      // LLVM's softmax-interleave strategy for the stage (instruction order
-      // only; about 1% off the backward, same bits)
-      __builtin_amdgcn_iglp_opt(2);
+      // S's chain, then dP's, with LLVM's MFMA / LDS-read interleave strategy
+      // for the stage (instruction order only: 1-2% off the backward against
+      // the two chains interleaved, same bits)
+      __builtin_amdgcn_iglp_opt(1);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+        sacc = mfma32x32x16(dual_row_read(qbuf, qrowp, 2 * ks + hf), kf[ks], sacc);
 #pragma unroll
       for (int ks = 0; ks < 8; ++ks) {
-        sacc = mfma32x32x16(dual_row_read(qbuf, qrowp, 2 * ks + hf), kf[ks], sacc);
         const u32x4 vb = *(const u32x4*)(Vt + row_offset<16>(vrow, 2 * ks + hf));
         dpacc = mfma32x32x16(dual_row_read(obuf, qrowp, 2 * ks + hf), vb, dpacc);
       }
